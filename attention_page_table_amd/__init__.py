@@ -1,0 +1,190 @@
+"""Python binding of the C ABI in include/tf.h (argument marshalling only).
+
+Every step of the path runs in the HIP library ``libtf.so`` built from ``csrc/``;
+torch supplies device memory and the current stream. There is no fallback: if the
+library is missing, importing the calls raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtf.so")
+
+TF_OK, TF_E_INVAL, TF_E_RANGE, TF_E_NOMEM, TF_E_UNSUPPORTED, TF_E_DEVICE = range(6)
+TF_LAT_BF16, TF_LAT_FP8E4M3_ROWSCALE = 0, 1
+TF_PLAN_ONE_WINDOW_FIRST, TF_PLAN_WINDOWS_FIRST = 0, 1
+
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class tf_geom(ctypes.Structure):
+    _fields_ = [("n_caches", _c_i32), ("page_rows", _c_i32), ("latent_dim", _c_i32), ("rope_dim", _c_i32),
+                ("pool_ratio", _c_i32), ("index_dim", _c_i32), ("lat_fmt", _c_i32)]
+
+
+class tf_budget(ctypes.Structure):
+    _fields_ = [("room_bytes", _c_i64), ("window_tokens", _c_i64), ("lookahead_rows", _c_i64),
+                ("fixed_bytes_per_stream", _c_i64), ("cache_cap_bytes", _c_i64), ("lanes", _c_i32),
+                ("policy", _c_i32)]
+
+
+class tf_plan(ctypes.Structure):
+    _fields_ = [("g", tf_geom),
+                ("lat_row_bytes", _c_i64), ("rope_row_bytes", _c_i64), ("pkey_row_bytes", _c_i64),
+                ("keys_per_page", _c_i64),
+                ("off_latent", _c_i64), ("off_scale", _c_i64), ("off_rope", _c_i64), ("off_pkey", _c_i64),
+                ("cache_block_bytes", _c_i64), ("page_bytes", _c_i64),
+                ("bytes_per_token", _c_i64), ("bytes_per_token_pages", _c_i64),
+                ("window_pages", _c_i64), ("n_windows", _c_i64), ("stream_pages", _c_i64),
+                ("total_pages", _c_i64), ("cache_bytes", _c_i64), ("fixed_bytes", _c_i64)]
+
+
+class tf_kv_view(ctypes.Structure):
+    _fields_ = [("pool", _vp), ("pt", _vp), ("pt_stride", _c_i32), ("n_streams", _c_i32), ("n_pages", _c_i32),
+                ("cache", _c_i32)]
+
+
+# name -> (restype, argtypes), in the order of include/tf.h
+SIGNATURES = {
+    "tf_kv_pool_plan": (_c_i32, [ctypes.POINTER(tf_geom), ctypes.POINTER(tf_budget), ctypes.POINTER(tf_plan)]),
+    "tf_prefill_chunk": (_c_i64, [_c_i64, _c_i64]),
+    "tf_latent_write": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i32,
+                                 _vp, _vp, _vp, _vp]),
+    "tf_indexer_logits": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32, _vp,
+                                   _c_i64, _vp, _vp]),
+    "tf_topk_blocks": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32]),
+    "tf_sparse_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
+                                    ctypes.c_float, _vp, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_attn_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
+    "tf_snapshot_copy": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, tf_kv_view, _c_i32, _vp, _vp, _c_i64, _vp]),
+    "tf_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtf.so; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_page_table_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class TFError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"tf status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != TF_OK:
+        raise TFError(status, lib().tf_last_error().decode())
+
+
+# ------------------------------------------------------------------ host calls
+def geom(n_caches=1, index_dim=128, fp8=False, rope_dim=64, page_rows=512, latent_dim=512, pool_ratio=4):
+    return tf_geom(n_caches, page_rows, latent_dim, rope_dim, pool_ratio, index_dim,
+                   TF_LAT_FP8E4M3_ROWSCALE if fp8 else TF_LAT_BF16)
+
+
+def kv_pool_plan(g: tf_geom, budget: tf_budget | None = None) -> tf_plan:
+    p = tf_plan()
+    _check(lib().tf_kv_pool_plan(ctypes.byref(g), ctypes.byref(budget) if budget is not None else None,
+                                 ctypes.byref(p)))
+    return p
+
+
+def prefill_chunk(history: int, remaining: int) -> int:
+    return int(lib().tf_prefill_chunk(history, remaining))
+
+
+# ------------------------------------------------------------------ device calls
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous and on the GPU"
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def view(pool, pt, pt_stride: int, n_pages: int, cache: int = 0, n_streams: int | None = None) -> tf_kv_view:
+    """pool: uint8 device tensor of n_pages * page_bytes; pt: int32 [streams, pt_stride] or None
+    (then stream b's page i is pool page b * pt_stride + i)."""
+    if pt is not None:
+        import torch
+        assert pt.dtype == torch.int32 and pt.dim() == 2 and pt.shape[1] == pt_stride
+        ns = pt.shape[0]
+    else:
+        ns = max(1, n_pages // pt_stride)
+    if n_streams is not None:
+        ns = n_streams
+    return tf_kv_view(_ptr(pool), _ptr(pt), pt_stride, ns, n_pages, cache)
+
+
+def latent_write(plan, dst, row_stream, row_pos, latent, rope, row_scale=None,
+                 pkey_stream=None, pkey_idx=None, pkeys=None, stream=None):
+    n_rows = 0 if row_stream is None else row_stream.numel()
+    n_pk = 0 if pkey_stream is None else pkey_stream.numel()
+    _check(lib().tf_latent_write(ctypes.byref(plan), dst, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(latent),
+                                 _ptr(row_scale), _ptr(rope), n_pk, _ptr(pkey_stream), _ptr(pkey_idx),
+                                 _ptr(pkeys), _stream(stream)))
+
+
+def indexer_logits(plan, keys, row_stream, row_pos, q, w, logits, n_valid=None, stream=None):
+    n_rows, H = w.shape
+    _check(lib().tf_indexer_logits(ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                   _ptr(w), H, _ptr(logits), logits.shape[1], _ptr(n_valid), _stream(stream)))
+
+
+def topk_workspace_bytes(n_rows: int, ld: int, k: int) -> int:
+    return int(lib().tf_topk_workspace_bytes(n_rows, ld, k))
+
+
+def topk_blocks(logits, n_valid, k: int, blocks, ws=None, stream=None):
+    n_rows, ld = logits.shape
+    need = topk_workspace_bytes(n_rows, ld, k)
+    if need and ws is None:
+        import torch
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    _check(lib().tf_topk_blocks(_ptr(logits), ld, n_rows, _ptr(n_valid), k, _ptr(blocks), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def attn_workspace_bytes(n_rows: int, n_heads: int, k: int) -> int:
+    return int(lib().tf_attn_workspace_bytes(n_rows, n_heads, k))
+
+
+def sparse_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, blocks, out, lse=None, ws=None,
+                    stream=None):
+    n_rows, n_heads = q.shape[0], q.shape[1]
+    k = blocks.shape[1]
+    need = attn_workspace_bytes(n_rows, n_heads, k)
+    if need and ws is None:
+        import torch
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().tf_sparse_mla_attn(ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                    n_heads, float(softmax_scale), _ptr(blocks), k, _ptr(out), _ptr(lse), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def snapshot_copy(plan, src, dst, src_stream, dst_stream, at: int, stream=None):
+    _check(lib().tf_snapshot_copy(ctypes.byref(plan), src, dst, src_stream.numel(), _ptr(src_stream),
+                                  _ptr(dst_stream), at, _stream(stream)))

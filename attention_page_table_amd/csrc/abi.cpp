@@ -1,0 +1,198 @@
+// The extern "C" entry points: argument validation on the host, then one launcher
+// per operation. Nothing here allocates, frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+
+namespace tf {
+
+static thread_local char g_err[512] = "";
+
+tf_status set_error(tf_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+tf_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(TF_E_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return TF_OK;
+}
+
+tf_status check_plan(const tf_plan* p) {
+  if (!p) return set_error(TF_E_INVAL, "plan must not be NULL (fill it with tf_kv_pool_plan)");
+  const tf_geom& g = p->g;
+  if (g.page_rows != kPageRows || g.latent_dim != kLatent || g.pool_ratio != kPoolRatio ||
+      (g.index_dim != 64 && g.index_dim != 128) || g.n_caches < 1 ||
+      (g.lat_fmt != TF_LAT_BF16 && g.lat_fmt != TF_LAT_FP8E4M3_ROWSCALE))
+    return set_error(TF_E_INVAL, "plan geometry is not one tf_kv_pool_plan produces");
+  if (p->page_bytes != p->cache_block_bytes * g.n_caches || p->page_bytes <= 0)
+    return set_error(TF_E_INVAL, "plan page_bytes is inconsistent: refill it with tf_kv_pool_plan");
+  return TF_OK;
+}
+
+tf_status check_view(const tf_plan* p, const tf_kv_view& v, const char* name) {
+  if (!v.pool) return set_error(TF_E_INVAL, "%s.pool must not be NULL", name);
+  if (v.n_pages < 1) return set_error(TF_E_INVAL, "%s.n_pages=%d, need >= 1", name, v.n_pages);
+  if (v.pt_stride < 1) return set_error(TF_E_INVAL, "%s.pt_stride=%d, need >= 1", name, v.pt_stride);
+  if (v.n_streams < 1) return set_error(TF_E_INVAL, "%s.n_streams=%d, need >= 1", name, v.n_streams);
+  if (v.cache < 0 || v.cache >= p->g.n_caches)
+    return set_error(TF_E_RANGE, "%s.cache=%d outside [0, %d)", name, v.cache, p->g.n_caches);
+  if (((uintptr_t)v.pool & 15) != 0) return set_error(TF_E_INVAL, "%s.pool must be 16-byte aligned", name);
+  return TF_OK;
+}
+
+DevView make_view(const tf_plan* p, const tf_kv_view& v) {
+  DevView d;
+  d.pool = (char*)v.pool;
+  d.pt = v.pt;
+  d.pt_stride = v.pt_stride;
+  d.n_streams = v.n_streams;
+  d.n_pages = v.n_pages;
+  d.page_bytes = p->page_bytes;
+  d.cache_off = (int64_t)v.cache * p->cache_block_bytes;
+  return d;
+}
+
+static bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
+
+}  // namespace tf
+
+using namespace tf;
+
+extern "C" const char* tf_last_error(void) { return g_err; }
+
+extern "C" tf_status tf_latent_write(const tf_plan* p, tf_kv_view dst, int32_t n_rows,
+                                     const int32_t* row_stream, const int32_t* row_pos,
+                                     const void* latent, const float* row_scale, const void* rope,
+                                     int32_t n_pkeys, const int32_t* pkey_stream,
+                                     const int32_t* pkey_idx, const void* pkeys, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, dst, "dst")) != TF_OK) return s;
+  if (n_rows < 0 || n_pkeys < 0) return set_error(TF_E_INVAL, "tf_latent_write: negative counts");
+  const bool fp8 = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE;
+  if (n_rows > 0) {
+    if (!row_stream || !row_pos || !latent)
+      return set_error(TF_E_INVAL, "tf_latent_write: row_stream, row_pos and latent are required");
+    if (p->g.rope_dim > 0 && !rope) return set_error(TF_E_INVAL, "tf_latent_write: rope is required");
+    if (fp8 && !row_scale) return set_error(TF_E_INVAL, "tf_latent_write: fp8 rows need row_scale");
+    if (!aligned16(latent) || (rope && !aligned16(rope)))
+      return set_error(TF_E_INVAL, "tf_latent_write: latent and rope must be 16-byte aligned");
+  }
+  if (n_pkeys > 0) {
+    if (!pkey_stream || !pkey_idx || !pkeys)
+      return set_error(TF_E_INVAL, "tf_latent_write: pkey_stream, pkey_idx and pkeys are required");
+    if (!aligned16(pkeys)) return set_error(TF_E_INVAL, "tf_latent_write: pkeys must be 16-byte aligned");
+  }
+  if (n_rows == 0 && n_pkeys == 0) return TF_OK;
+  return launch_latent_write(p, make_view(p, dst), n_rows, row_stream, row_pos, latent, row_scale, rope,
+                             n_pkeys, pkey_stream, pkey_idx, pkeys, (hipStream_t)stream);
+}
+
+extern "C" tf_status tf_snapshot_copy(const tf_plan* p, tf_kv_view src, tf_kv_view dst,
+                                      int32_t n_streams, const int32_t* src_stream,
+                                      const int32_t* dst_stream, int64_t at, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  src.cache = 0;
+  dst.cache = 0;
+  if ((s = check_view(p, src, "src")) != TF_OK) return s;
+  if ((s = check_view(p, dst, "dst")) != TF_OK) return s;
+  if (n_streams < 0) return set_error(TF_E_INVAL, "tf_snapshot_copy: n_streams < 0");
+  if (at < 0 || at % kPoolRatio != 0)
+    return set_error(TF_E_INVAL, "tf_snapshot_copy: at=%lld must be a non-negative multiple of 4",
+                     (long long)at);
+  const int64_t pages = (at + kPageRows - 1) / kPageRows;
+  if (pages > src.pt_stride || pages > dst.pt_stride)
+    return set_error(TF_E_RANGE, "tf_snapshot_copy: at=%lld needs %lld pages, the tables hold %d and %d",
+                     (long long)at, (long long)pages, src.pt_stride, dst.pt_stride);
+  if (n_streams == 0 || at == 0) return TF_OK;
+  if (!src_stream || !dst_stream)
+    return set_error(TF_E_INVAL, "tf_snapshot_copy: src_stream and dst_stream are required");
+  return launch_snapshot(p, src, dst, n_streams, src_stream, dst_stream, at, (hipStream_t)stream);
+}
+
+extern "C" tf_status tf_indexer_logits(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
+                                       const int32_t* row_stream, const int32_t* row_pos,
+                                       const void* q, const float* w, int32_t n_heads, float* logits,
+                                       int64_t ld, int32_t* n_valid, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, keys, "keys")) != TF_OK) return s;
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_indexer_logits: n_rows < 0");
+  if (ld < 1 || ld > (1LL << 30)) return set_error(TF_E_RANGE, "tf_indexer_logits: ld=%lld", (long long)ld);
+  if (n_heads != 4 && n_heads != 8 && n_heads != 16)
+    return set_error(TF_E_UNSUPPORTED, "tf_indexer_logits: n_heads=%d, built for 4, 8 or 16", n_heads);
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !w || !logits)
+    return set_error(TF_E_INVAL, "tf_indexer_logits: row_stream, row_pos, q, w and logits are required");
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_indexer_logits: q must be 16-byte aligned");
+  return launch_indexer(p, make_view(p, keys), n_rows, row_stream, row_pos, q, w, n_heads, logits, ld,
+                        n_valid, (hipStream_t)stream);
+}
+
+extern "C" size_t tf_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k) {
+  if (n_rows <= 0 || ld <= 0 || k <= 0) return 0;
+  return topk_ws_bytes(n_rows, ld, k);
+}
+
+extern "C" tf_status tf_topk_blocks(const float* logits, int64_t ld, int32_t n_rows,
+                                    const int32_t* n_valid, int32_t k, int32_t* blocks, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  clear_error();
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_topk_blocks: n_rows < 0");
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_topk_blocks: k=%d, need 1..2048", k);
+  if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_topk_blocks: ld=%lld", (long long)ld);
+  if (n_rows == 0) return TF_OK;
+  if (!logits || !blocks) return set_error(TF_E_INVAL, "tf_topk_blocks: logits and blocks are required");
+  const size_t need = topk_ws_bytes(n_rows, ld, k);
+  if (need == (size_t)-1)
+    return set_error(TF_E_UNSUPPORTED, "tf_topk_blocks: ld=%lld with k=%d exceeds the blocked merge",
+                     (long long)ld, k);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return set_error(TF_E_INVAL, "tf_topk_blocks: workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  return launch_topk(logits, ld, n_rows, n_valid, k, blocks, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {
+  if (n_rows <= 0 || n_heads <= 0 || k <= 0) return 0;
+  return attn_ws_bytes(n_rows, n_heads, k);
+}
+
+extern "C" tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
+                                        const int32_t* row_stream, const int32_t* row_pos,
+                                        const void* q, int32_t n_heads, float softmax_scale,
+                                        const int32_t* blocks, int32_t k, float* out, float* lse,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, kv, "kv")) != TF_OK) return s;
+  if (p->g.rope_dim != kRope)
+    return set_error(TF_E_UNSUPPORTED, "tf_sparse_mla_attn: needs the 64-value rope plane");
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_sparse_mla_attn: n_rows < 0");
+  if (n_heads < 1 || n_heads > 32)
+    return set_error(TF_E_UNSUPPORTED, "tf_sparse_mla_attn: n_heads=%d, built for 1..32", n_heads);
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_sparse_mla_attn: k=%d, need 1..2048", k);
+  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f)
+    return set_error(TF_E_INVAL, "tf_sparse_mla_attn: softmax_scale must be > 0");
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !blocks || !out)
+    return set_error(TF_E_INVAL, "tf_sparse_mla_attn: row_stream, row_pos, q, blocks and out are required");
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_sparse_mla_attn: q must be 16-byte aligned");
+  const size_t need = attn_ws_bytes(n_rows, n_heads, k);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return set_error(TF_E_INVAL, "tf_sparse_mla_attn: workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  return launch_attn(p, make_view(p, kv), n_rows, row_stream, row_pos, q, n_heads, softmax_scale, blocks,
+                     k, out, lse, ws, ws_bytes, (hipStream_t)stream);
+}

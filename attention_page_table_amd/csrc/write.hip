@@ -1,0 +1,179 @@
+// Latent / rope / pooled-key row writes through the page table, and the snapshot
+// copy of a stream's first `at` rows. Both are byte copies, bound by HBM.
+//
+// [#1142, "GLM declares a kv_pool.Layout"]: the writes take the page table; a
+// null table keeps contiguous rows. [#1142, "Proposal" piece 1]: a kept state
+// copies each cache's first at rows and the pooled keys up to at.
+#include "common.h"
+
+namespace tf {
+
+struct WriteArgs {
+  DevView v;
+  int32_t n_rows, n_pkeys;
+  const int32_t* row_stream;
+  const int32_t* row_pos;
+  const uint4* latent;   // n_rows * lat16 vectors
+  const float* scale;    // fp8 only
+  const uint4* rope;     // n_rows * rope16 vectors
+  const int32_t* pkey_stream;
+  const int32_t* pkey_idx;
+  const uint4* pkeys;    // n_pkeys * key16 vectors
+  int32_t lat16, rope16, key16;  // 16-byte vectors per latent row / rope row / key
+  int64_t off_scale, off_rope, off_pkey;
+  int32_t lat_row_bytes, rope_row_bytes, pkey_row_bytes;
+  int32_t row_blocks;    // blocks that write rows; the rest write keys
+};
+
+constexpr int kRowsPerBlock = 4;   // 64 threads per row
+constexpr int kKeysPerBlock = 16;  // 16 threads per key
+
+__global__ __launch_bounds__(256) void latent_write_kernel(WriteArgs a) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < a.row_blocks) {
+    const int r = blockIdx.x * kRowsPerBlock + tid / 64;
+    const int lane = tid % 64;
+    if (r >= a.n_rows) return;
+    const int b = a.row_stream[r];
+    const int t = a.row_pos[r];
+    if (t < 0) return;
+    const int page = page_of(a.v, b, t / kPageRows);
+    if (page < 0) return;
+    char* blk = cache_block(a.v, page);
+    const int slot = t % kPageRows;
+    uint4* dl = (uint4*)(blk + (int64_t)slot * a.lat_row_bytes);
+    const uint4* sl = a.latent + (int64_t)r * a.lat16;
+    for (int i = lane; i < a.lat16; i += 64) dl[i] = sl[i];
+    if (a.rope16 > 0) {
+      uint4* dr = (uint4*)(blk + a.off_rope + (int64_t)slot * a.rope_row_bytes);
+      const uint4* sr = a.rope + (int64_t)r * a.rope16;
+      for (int i = lane; i < a.rope16; i += 64) dr[i] = sr[i];
+    }
+    if (a.scale && lane == 0) *(float*)(blk + a.off_scale + 4LL * slot) = a.scale[r];
+  } else {
+    const int kk = (blockIdx.x - a.row_blocks) * kKeysPerBlock + tid / 16;
+    const int lane = tid % 16;
+    if (kk >= a.n_pkeys) return;
+    const int b = a.pkey_stream[kk];
+    const int j = a.pkey_idx[kk];
+    if (j < 0) return;
+    const int page = page_of(a.v, b, j / kKeysPerPage);
+    if (page < 0) return;
+    uint4* dk = (uint4*)(cache_block(a.v, page) + a.off_pkey + (int64_t)(j % kKeysPerPage) * a.pkey_row_bytes);
+    const uint4* sk = a.pkeys + (int64_t)kk * a.key16;
+    for (int i = lane; i < a.key16; i += 16) dk[i] = sk[i];
+  }
+}
+
+tf_status launch_latent_write(const tf_plan* p, const DevView& v, int32_t n_rows,
+                              const int32_t* row_stream, const int32_t* row_pos, const void* latent,
+                              const float* row_scale, const void* rope, int32_t n_pkeys,
+                              const int32_t* pkey_stream, const int32_t* pkey_idx, const void* pkeys,
+                              hipStream_t st) {
+  WriteArgs a;
+  a.v = v;
+  a.n_rows = n_rows;
+  a.n_pkeys = n_pkeys;
+  a.row_stream = row_stream;
+  a.row_pos = row_pos;
+  a.latent = (const uint4*)latent;
+  a.scale = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE ? row_scale : nullptr;
+  a.rope = (const uint4*)rope;
+  a.pkey_stream = pkey_stream;
+  a.pkey_idx = pkey_idx;
+  a.pkeys = (const uint4*)pkeys;
+  a.lat16 = (int32_t)(p->lat_row_bytes / 16);
+  a.rope16 = (int32_t)(p->rope_row_bytes / 16);
+  a.key16 = (int32_t)(p->pkey_row_bytes / 16);
+  a.off_scale = p->off_scale;
+  a.off_rope = p->off_rope;
+  a.off_pkey = p->off_pkey;
+  a.lat_row_bytes = (int32_t)p->lat_row_bytes;
+  a.rope_row_bytes = (int32_t)p->rope_row_bytes;
+  a.pkey_row_bytes = (int32_t)p->pkey_row_bytes;
+  a.row_blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int key_blocks = (n_pkeys + kKeysPerBlock - 1) / kKeysPerBlock;
+  hipLaunchKernelGGL(latent_write_kernel, dim3(a.row_blocks + key_blocks), dim3(256), 0, st, a);
+  return launch_status("tf_latent_write");
+}
+
+// ---- snapshot -----------------------------------------------------------------------
+
+struct SnapArgs {
+  DevView src, dst;   // cache_off = 0: every cache of a page is copied
+  const int32_t* src_stream;
+  const int32_t* dst_stream;
+  int64_t at;
+  int32_t n_caches;
+  int64_t cache_block_bytes;
+  int64_t off_scale, off_rope, off_pkey;
+  int32_t lat_row_bytes, rope_row_bytes, pkey_row_bytes;
+  int32_t has_scale;
+};
+
+constexpr int kSnapUnitsPerBlock = 4096;  // 64 KiB of 16-byte units per block
+
+// grid: x = chunk of a page's bytes, y = page index * n_caches + cache, z = stream pair
+__global__ __launch_bounds__(256) void snapshot_kernel(SnapArgs a) {
+  const int pidx = blockIdx.y / a.n_caches;
+  const int c = blockIdx.y % a.n_caches;
+  const int bs = a.src_stream[blockIdx.z];
+  const int bd = a.dst_stream[blockIdx.z];
+  const int ps = page_of(a.src, bs, pidx);
+  const int pd = page_of(a.dst, bd, pidx);
+  if (ps < 0 || pd < 0) return;
+  const int64_t row0 = (int64_t)pidx * kPageRows;
+  int64_t nr = a.at - row0;
+  if (nr > kPageRows) nr = kPageRows;
+  const int64_t nk = nr / kPoolRatio;
+  // four contiguous ranges of the cache block, in 16-byte units
+  const int64_t u_lat = nr * a.lat_row_bytes / 16;
+  const int64_t u_sc = a.has_scale ? nr * 4 / 16 : 0;
+  const int64_t u_rope = nr * a.rope_row_bytes / 16;
+  const int64_t u_key = nk * a.pkey_row_bytes / 16;
+  const int64_t total = u_lat + u_sc + u_rope + u_key;
+  const char* s = cache_block(a.src, ps) + (int64_t)c * a.cache_block_bytes;
+  char* d = cache_block(a.dst, pd) + (int64_t)c * a.cache_block_bytes;
+  const int64_t u0 = (int64_t)blockIdx.x * kSnapUnitsPerBlock;
+  const int64_t u1 = u0 + kSnapUnitsPerBlock < total ? u0 + kSnapUnitsPerBlock : total;
+  for (int64_t u = u0 + threadIdx.x; u < u1; u += 256) {
+    int64_t off;
+    if (u < u_lat) off = u * 16;
+    else if (u < u_lat + u_sc) off = a.off_scale + (u - u_lat) * 16;
+    else if (u < u_lat + u_sc + u_rope) off = a.off_rope + (u - u_lat - u_sc) * 16;
+    else off = a.off_pkey + (u - u_lat - u_sc - u_rope) * 16;
+    *(uint4*)(d + off) = *(const uint4*)(s + off);
+  }
+}
+
+tf_status launch_snapshot(const tf_plan* p, const tf_kv_view& src, const tf_kv_view& dst,
+                          int32_t n_streams, const int32_t* src_stream, const int32_t* dst_stream,
+                          int64_t at, hipStream_t st) {
+  SnapArgs a;
+  a.src = make_view(p, src);
+  a.dst = make_view(p, dst);
+  a.src.cache_off = 0;
+  a.dst.cache_off = 0;
+  a.src_stream = src_stream;
+  a.dst_stream = dst_stream;
+  a.at = at;
+  a.n_caches = p->g.n_caches;
+  a.cache_block_bytes = p->cache_block_bytes;
+  a.off_scale = p->off_scale;
+  a.off_rope = p->off_rope;
+  a.off_pkey = p->off_pkey;
+  a.lat_row_bytes = (int32_t)p->lat_row_bytes;
+  a.rope_row_bytes = (int32_t)p->rope_row_bytes;
+  a.pkey_row_bytes = (int32_t)p->pkey_row_bytes;
+  a.has_scale = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE;
+  const int64_t pages = (at + kPageRows - 1) / kPageRows;
+  const int64_t max_units = p->cache_block_bytes / 16;
+  const int64_t chunks = (max_units + kSnapUnitsPerBlock - 1) / kSnapUnitsPerBlock;
+  if (pages * p->g.n_caches > 65535 || n_streams > 65535)
+    return set_error(TF_E_RANGE, "tf_snapshot_copy: too many pages or streams for one launch");
+  hipLaunchKernelGGL(snapshot_kernel, dim3((unsigned)chunks, (unsigned)(pages * p->g.n_caches), n_streams),
+                     dim3(256), 0, st, a);
+  return launch_status("tf_snapshot_copy");
+}
+
+}  // namespace tf

@@ -1,0 +1,135 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry point that
+include/tf.h declares, its host-only plan and chunk rule agree with the oracle, and
+argument validation refuses bad calls before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_page_table_amd as tf
+import oracle
+from oracle.plan import ONE_WINDOW_FIRST, WINDOWS_FIRST, PlanNoMem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tf.h")
+MiB, GiB = 1 << 20, 1 << 30
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tf_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = tf.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tf.SIGNATURES), "binding and header list different entry points"
+
+
+@pytest.mark.parametrize("n_caches,index_dim,fp8,rope", [(1, 64, False, 64), (12, 128, False, 64),
+                                                         (12, 128, True, 64), (12, 128, False, 0),
+                                                         (3, 128, True, 0)])
+def test_layout_matches_oracle(n_caches, index_dim, fp8, rope):
+    p = tf.kv_pool_plan(tf.geom(n_caches, index_dim, fp8, rope_dim=rope))
+    g = oracle.Geom(n_caches=n_caches, index_dim=index_dim, fp8=fp8, rope_dim=rope)
+    L = oracle.block_layout(g)
+    assert (p.off_latent, p.off_scale, p.off_rope, p.off_pkey) == (L.off_latent, L.off_scale, L.off_rope, L.off_pkey)
+    assert p.cache_block_bytes == L.block and p.page_bytes == oracle.page_bytes(g)
+    assert p.bytes_per_token == oracle.bytes_per_token(g)
+    assert (p.lat_row_bytes, p.rope_row_bytes, p.pkey_row_bytes) == (L.lat_row, L.rope_row, L.pkey_row)
+
+
+def test_pages_figures_through_the_abi():
+    p = tf.kv_pool_plan(tf.geom(12, 128, rope_dim=0))
+    assert p.bytes_per_token_pages == 13056
+    b = tf.tf_budget(int(15.2 * GiB), 1048576, 1, 176 * MiB, 16 * GiB, 8, tf.TF_PLAN_ONE_WINDOW_FIRST)
+    q = tf.kv_pool_plan(tf.geom(12, 128, rope_dim=0), b)
+    assert (q.window_pages, q.total_pages) == (2049, 2056)
+
+
+@pytest.mark.parametrize("policy", [ONE_WINDOW_FIRST, WINDOWS_FIRST])
+def test_budget_matches_oracle(policy):
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        nc = int(rng.integers(1, 13))
+        g = oracle.Geom(n_caches=nc, index_dim=128, rope_dim=int(rng.choice([0, 64])), fp8=bool(rng.integers(2)))
+        room = int(rng.integers(1, 200)) * GiB + int(rng.integers(0, GiB))
+        win = int(rng.integers(1, 2_000_000))
+        look = int(rng.integers(0, 3))
+        fixed = int(rng.integers(0, 400)) * MiB
+        cap = int(rng.integers(0, 32)) * GiB
+        lanes = int(rng.integers(1, 17))
+        b = tf.tf_budget(room, win, look, fixed, cap, lanes, policy)
+        try:
+            want = oracle.kv_pool_plan(g, room, win, look, fixed, cap, lanes, policy)
+        except PlanNoMem:
+            with pytest.raises(tf.TFError) as e:
+                tf.kv_pool_plan(tf.geom(nc, 128, g.fp8, g.rope_dim), b)
+            assert e.value.status == tf.TF_E_NOMEM and "room" in str(e.value)
+            continue
+        got = tf.kv_pool_plan(tf.geom(nc, 128, g.fp8, g.rope_dim), b)
+        assert (got.window_pages, got.n_windows, got.stream_pages, got.total_pages, got.cache_bytes,
+                got.fixed_bytes) == (want.window_pages, want.n_windows, want.stream_pages, want.total_pages,
+                                     want.cache_bytes, want.fixed_bytes)
+
+
+def test_chunk_rule_matches_oracle():
+    for L in list(range(0, 3000, 7)) + list(range(90_000, 900_000, 997)):
+        assert tf.prefill_chunk(L, 10**9) == oracle.chunk_size(L)
+    assert tf.prefill_chunk(389_888, 112) == 112
+    assert tf.prefill_chunk(5, 0) == 0
+    s, L = [], 0
+    while L < 390_000:
+        c = tf.prefill_chunk(L, 390_000 - L)
+        s.append((L, c))
+        L += c
+    assert s == oracle.chunk_schedule(390_000)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_validation_refuses_before_launch():
+    L = tf.lib()
+    p = tf.kv_pool_plan(tf.geom(1, 64))
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+    v = tf.tf_kv_view(fake, None, 4, 4, 16, 0)
+    # at not a multiple of 4
+    assert L.tf_snapshot_copy(ctypes.byref(p), v, v, 1, fake, fake, 6, None) == tf.TF_E_INVAL
+    assert "multiple of 4" in L.tf_last_error().decode()
+    # at beyond the tables
+    assert L.tf_snapshot_copy(ctypes.byref(p), v, v, 1, fake, fake, 4 * 512 + 4, None) == tf.TF_E_RANGE
+    # cache outside the plan
+    bad = tf.tf_kv_view(fake, None, 4, 4, 16, 3)
+    assert L.tf_indexer_logits(ctypes.byref(p), bad, 1, fake, fake, fake, fake, 4, fake, 16, None,
+                               None) == tf.TF_E_RANGE
+    # heads the indexer is not built for
+    assert L.tf_indexer_logits(ctypes.byref(p), v, 1, fake, fake, fake, fake, 5, fake, 16, None,
+                               None) == tf.TF_E_UNSUPPORTED
+    # k out of range, missing workspace
+    assert L.tf_topk_blocks(fake, 100, 1, None, 0, fake, None, 0, None) == tf.TF_E_RANGE
+    assert L.tf_topk_blocks(fake, 1 << 20, 1, None, 512, fake, None, 0, None) == tf.TF_E_INVAL
+    assert "workspace" in L.tf_last_error().decode()
+    assert L.tf_sparse_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 33, 1.0, fake, 64, fake, None, None, 0,
+                                None) == tf.TF_E_UNSUPPORTED
+    assert L.tf_sparse_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, -1.0, fake, 64, fake, None, None, 0,
+                                None) == tf.TF_E_INVAL
+    # null plan, null pool
+    assert L.tf_latent_write(None, v, 1, fake, fake, fake, None, fake, 0, None, None, None, None) == tf.TF_E_INVAL
+    nv = tf.tf_kv_view(None, None, 4, 4, 16, 0)
+    assert L.tf_latent_write(ctypes.byref(p), nv, 1, fake, fake, fake, None, fake, 0, None, None, None,
+                             None) == tf.TF_E_INVAL
+    # bad geometry
+    with pytest.raises(tf.TFError) as e:
+        tf.kv_pool_plan(tf.geom(1, 96))
+    assert e.value.status == tf.TF_E_UNSUPPORTED
+    # a successful call clears the message
+    assert L.tf_topk_blocks(fake, 100, 0, None, 4, fake, None, 0, None) == tf.TF_OK
+    assert L.tf_last_error().decode() == ""

@@ -1,0 +1,242 @@
+"""GPU parity on the tiny workload (2 streams x 2,048 tokens, 16-page pool, 8 heads,
+top-64): every step through the C ABI, element by element against the oracle.
+Sizes span several tiles and ragged tails; edge cases included."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_page_table_amd as tf
+from oracle import PoolImage, Geom, topk_blocks
+from oracle import workload as ow
+from oracle.layout import snapshot_copy
+from synth import TAG_LATENT, bf16_values, e4m3_codes, fp8_row_scales, TAG_LAT8, TAG_SCALE8
+from synth.configs import tiny, ROW, rid
+from synth.device import alloc_pool, populate, query_inputs, fill_bf16, fill_e4m3, fill_scale8, NAN16
+from tests.gpu_common import (bf16_host, check_attention, check_logits, check_topk_against_oracle, host,
+                              logits_bound, topk_on_values)
+
+pytestmark = pytest.mark.gpu
+SCALES = [1.0 / math.sqrt(576.0), 24.0]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny_pool():
+    wl = tiny(0)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    torch.cuda.synchronize()
+    return wl, plan, P
+
+
+def oracle_image(wl, fp8=False):
+    g = Geom(n_caches=wl.n_caches, index_dim=wl.Dk, fp8=fp8)
+    img = PoolImage(g, wl.n_pages, fill=NAN16)
+    for b in range(wl.n_streams):
+        L = wl.lengths[b]
+        if fp8:
+            codes, sc, rope = wl.latent_fp8(0, b, np.arange(L))
+            for t in range(L):
+                img.write_row(wl.pt, wl.pt_stride, b, t, 0, codes[t], rope[t], sc[t])
+        else:
+            bits = wl.latent_bits(0, b, np.arange(L))
+            for t in range(L):
+                img.write_row(wl.pt, wl.pt_stride, b, t, 0, bits[t, :512], bits[t, 512:])
+        kb = wl.pkey_bits(0, b, np.arange(wl.n_keys(b)))
+        for j in range(wl.n_keys(b)):
+            img.write_pkey(wl.pt, wl.pt_stride, b, j, 0, kb[j])
+    return img
+
+
+def test_device_generator_matches_host():
+    _log("generator: bf16, e4m3 and scale fills against numpy")
+    n = 100_003
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    fill_bf16(out, n // 7, 7, 3, TAG_LATENT, 12345, 11, 576)
+    m = (n // 7) * 7
+    idx = 12345 + (np.arange(m) // 7) * 11 + np.arange(m) % 7
+    assert np.array_equal(host(out.view(torch.int16))[:m].view(np.uint16), bf16_values(3, TAG_LATENT, idx, 576))
+    o8 = torch.empty(m, dtype=torch.uint8, device="cuda")
+    fill_e4m3(o8, n // 7, 7, 3, TAG_LAT8, 12345, 11)
+    assert np.array_equal(host(o8), e4m3_codes(3, TAG_LAT8, idx))
+    sc = torch.empty(1000, dtype=torch.float32, device="cuda")
+    fill_scale8(sc, 1000, 3, TAG_SCALE8, 77)
+    assert np.array_equal(host(sc), fp8_row_scales(3, TAG_SCALE8, 77 + np.arange(1000)))
+
+
+def test_write_bytes_exact(tiny_pool):
+    _log("write: pool bytes against the oracle's pool image (tiny)")
+    wl, plan, P = tiny_pool
+    img = oracle_image(wl)
+    assert np.array_equal(host(P.pool), img.buf)
+
+
+def test_snapshot_bytes_exact(tiny_pool):
+    _log("snapshot: first at rows into fresh pages (tiny)")
+    wl, plan, P = tiny_pool
+    at = 1540  # not a page multiple: a partial last page
+    dst = torch.empty(4 * plan.page_bytes, dtype=torch.uint8, device="cuda")
+    dst.view(torch.int16).fill_(NAN16)
+    dpt = torch.tensor([[2, 0, 3, 1]], dtype=torch.int32, device="cuda")
+    src_s = torch.tensor([1], dtype=torch.int32, device="cuda")
+    dst_s = torch.tensor([0], dtype=torch.int32, device="cuda")
+    tf.snapshot_copy(plan, P.view(), tf.view(dst, dpt, 4, 4), src_s, dst_s, at)
+    torch.cuda.synchronize()
+    img = oracle_image(wl)
+    dimg = PoolImage(img.g, 4, fill=NAN16)
+    snapshot_copy(img, wl.pt, wl.pt_stride, dimg, host(dpt), 4, [1], [0], at)
+    assert np.array_equal(host(dst), dimg.buf)
+    with pytest.raises(tf.TFError):
+        tf.snapshot_copy(plan, P.view(), tf.view(dst, dpt, 4, 4), src_s, dst_s, 6)
+
+
+def run_step(wl, plan, view, rows, ld, scale, k=None):
+    k = k or wl.k
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    R = len(rows)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, view, rs, rp, iq, w, logits, n_valid=nv)
+    blocks = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    tf.topk_blocks(logits, nv, k, blocks)
+    out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+    tf.sparse_mla_attn(plan, view, rs, rp, q, scale, blocks, out, lse)
+    torch.cuda.synchronize()
+    return host(logits), host(nv), host(blocks), host(out), host(lse)
+
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_full_step_against_oracle(tiny_pool, scale):
+    _log(f"step: indexer -> top-k -> attention, tiny, scale {scale:.4f}")
+    wl, plan, P = tiny_pool
+    rows = wl.rows
+    ld = 512
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, ld, scale)
+    ref_l = ow.logits(wl, 0, rows, ld)
+    check_logits(lg, ref_l, logits_bound(wl, 0, rows, ld), "tiny")
+    assert np.array_equal(nv, ow.n_valid(rows, ld))
+    # top-k on the GPU's own logits is exact
+    assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+    check_topk_against_oracle(blk, ref_l, nv, wl.k)
+    ro, rl = ow.attention(wl, 0, rows, blk, scale)
+    check_attention(out, lse, ro, rl, "tiny")
+
+
+def test_paged_equals_contiguous_bitwise(tiny_pool):
+    _log("paged == contiguous window, bit for bit (tiny)")
+    wl, plan, P = tiny_pool
+    contig = torch.empty(8 * plan.page_bytes, dtype=torch.uint8, device="cuda")
+    contig.view(torch.int16).fill_(NAN16)
+    # copy each stream's pages into window order with the snapshot (rows [0, 2048))
+    s = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    tf.snapshot_copy(plan, P.view(), tf.view(contig, None, 4, 8), s, s, 2048)
+    a = run_step(wl, plan, P.view(), wl.rows, 512, 24.0)
+    b = run_step(wl, plan, tf.view(contig, None, 4, 8), wl.rows, 512, 24.0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_shuffled_pages_same_bits():
+    _log("another page permutation gives the same bits (tiny)")
+    wl1 = tiny(0)
+    wl2 = tiny(0)
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(16).astype(np.int32)
+    wl2.pt = perm[:8].reshape(2, 4)
+    outs = []
+    for wl in (wl1, wl2):
+        plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+        P = alloc_pool(wl, plan)
+        populate(P)
+        outs.append(run_step(wl, plan, P.view(), wl.rows, 512, 24.0))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
+def test_decode_row_equals_chunk_last_row(tiny_pool):
+    _log("decode row == last row of the prefill chunk (tiny)")
+    wl, plan, P = tiny_pool
+    dec = run_step(wl, plan, P.view(), [(0, 2047)], 512, 24.0)
+    chunk = run_step(wl, plan, P.view(), [(0, t) for t in range(1792, 2048)], 512, 24.0)
+    assert np.array_equal(dec[0][0], chunk[0][-1])
+    assert np.array_equal(dec[2][0], chunk[2][-1])
+    check_attention(dec[3], dec[4], chunk[3][-1:], chunk[4][-1:], "decode vs chunk")
+
+
+def test_topk_takes_all_and_dense_equivalence(tiny_pool):
+    _log("top-k >= visible blocks: attention equals dense causal attention (tiny)")
+    wl, plan, P = tiny_pool
+    rows = [(0, 0), (0, 3), (0, 4), (1, 37), (1, 255), (0, 511)]   # n_c = 1, 1, 2, 10, 64, 128
+    ld = 128
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, ld, 24.0, k=128)
+    for r, (b, t) in enumerate(rows):
+        nc = t // 4 + 1
+        assert blk[r, :nc].tolist() == list(range(nc)) and np.all(blk[r, nc:] == -1)
+    from oracle.attention import sparse_mla_row
+    from synth import bf16_to_f64
+    q = bf16_to_f64(wl.q_bits(0, rows))
+    for r, (b, t) in enumerate(rows):
+        o, l = sparse_mla_row(q[r], ow.rows_reader(wl, 0, b), list(range(t // 4 + 1)), t, 24.0)
+        check_attention(out[r:r + 1], lse[r:r + 1], o[None], l[None], f"dense row {r}")
+
+
+def test_topk_edge_cases():
+    _log("top-k: ties, signed zeros, ragged rows, k > n_valid, single and blocked modes")
+    rng = np.random.default_rng(5)
+    for ld, R, k in [(300, 5, 64), (5000, 3, 512), (40000, 4, 512), (4096, 600, 100), (20000, 600, 512)]:
+        v = np.round(rng.standard_normal((R, ld)), 1).astype(np.float32)    # many ties
+        v[0, :50] = -0.0
+        v[0, 50:100] = 0.0
+        nv = rng.integers(1, ld + 1, size=R).astype(np.int32)
+        nv[0] = ld
+        nv[-1] = min(ld, k - 1) if k > 1 else 1                               # fewer than k visible
+        lg = torch.from_numpy(v).cuda()
+        nvt = torch.from_numpy(nv).cuda()
+        blk = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        tf.topk_blocks(lg, nvt, k, blk)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(blk), topk_on_values(v, nv, k)), (ld, R, k)
+    # all equal values
+    lg = torch.zeros((2, 10000), dtype=torch.float32, device="cuda")
+    blk = torch.empty((2, 512), dtype=torch.int32, device="cuda")
+    tf.topk_blocks(lg, None, 512, blk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(blk), np.tile(np.arange(512), (2, 1)))
+
+
+def test_empty_and_degenerate(tiny_pool):
+    _log("degenerate calls: zero rows, blocks all -1")
+    wl, plan, P = tiny_pool
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    tf.latent_write(plan, P.view(), e, e, torch.empty((0, 512), dtype=torch.bfloat16, device="cuda"),
+                    torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    rs, rp, iq, w, q = query_inputs(wl, 0, [(0, 100), (1, 2047)])
+    blocks = torch.full((2, 64), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((2, wl.Hq, 512), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.zeros((2, wl.Hq), dtype=torch.float32, device="cuda")
+    tf.sparse_mla_attn(plan, P.view(), rs, rp, q, 1.0, blocks, out, lse)
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
+
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_fp8_rows(scale):
+    _log(f"fp8 rows: write bytes and attention with in-kernel dequant (tiny, scale {scale:.4f})")
+    wl = tiny(1)
+    wl.fp8 = True
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    torch.cuda.synchronize()
+    img = oracle_image(wl, fp8=True)
+    assert np.array_equal(host(P.pool), img.buf)
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), wl.rows, 512, scale)
+    ro, rl = ow.attention(wl, 0, wl.rows, blk, scale)
+    check_attention(out, lse, ro, rl, "fp8 tiny")
