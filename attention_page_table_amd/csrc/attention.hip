@@ -8,19 +8,25 @@
 // Per row t and head h over S = {s <= t : s/4 selected}:
 //   z_s = scale * q_h . [c_s ; r_s],  out_h = sum_s softmax(z)_s c_s,  lse_h.
 //
-// Design (gfx950, one workgroup of 4 waves per (row, split of its block list)):
+// Design (gfx950). One workgroup of 4 waves takes (row, group of HG heads,
+// split of the row's block list):
+//   * the workgroup's token table (page and slot of every selected token) is
+//     built once, in LDS;
 //   * 32-token tiles (8 blocks; a block never straddles a 512-row page) are
-//     gathered with 16-byte coalesced loads into an LDS tile [32][576] bf16;
-//     fp8 rows are widened to bf16 exactly and their scales kept per token.
-//   * S = Q K^T on v_mfma_f32_32x32x16_bf16 with the 32 heads as M; the 36
-//     k-steps (32 latent + 4 rope) are split over the 4 waves and the partial
-//     S tiles summed through LDS. The fp8 row scale multiplies the latent part.
-//   * Online softmax in fp32 (exp2 domain).
+//     gathered with 16-byte coalesced loads; the next tile's loads are issued
+//     into registers before the current tile is computed; fp8 rows are widened
+//     to bf16 exactly (the row scale is kept per token);
+//   * S = Q K^T on MFMA with the heads as M (HG = 32: 32x32x16; HG = 16:
+//     16x16x32), the 576-long contraction split over waves and summed through
+//     LDS; the fp8 row scale multiplies the latent part of S;
+//   * online softmax in fp32 (exp2 domain);
 //   * O += P V on MFMA with P as a bf16 hi + lo pair (16 significant bits) and
-//     V read from the LDS tile transposed; each wave owns 128 of the 512 output
-//     columns in 64 accumulator registers. The fp8 scale is folded into P.
-//   * Rows with few tokens per CU (decode) split their block list; partial
-//     (O, max, sum) go to the workspace and a small merge kernel combines them.
+//     V read from the LDS tile transposed; each wave owns 128 output columns;
+//     the fp8 row scale is folded into P.
+//   Decode rows (few rows, many CUs) split their block list and, with HG = 16,
+//   their heads; the two head groups of one split sit on the same XCD (workgroup
+//   i runs on XCD i mod 8) so the second gather hits L2. Partial (O, max, sum)
+//   go to the workspace and a merge kernel combines them.
 #include <math.h>
 
 #include "common.h"
@@ -28,7 +34,10 @@
 namespace tf {
 
 constexpr int kTileTok = 32;
-constexpr int kRS = kRow + 8;  // LDS row stride in bf16 (1,168 bytes)
+constexpr int kRS = kRow + 8;       // LDS row stride in bf16 (1,168 bytes)
+constexpr int kMaxWgTok = 2048;     // tokens one workgroup may own (k <= 512 blocks)
+constexpr int kMasked = -1;         // token table: not attended
+constexpr int kUnreadable = -2;     // token table: selected but the table names no page
 
 struct AttnArgs {
   DevView v;
@@ -42,23 +51,24 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   const int32_t* blocks;
   int32_t k;
-  int32_t nsplit, slots_per_split;
+  int32_t nsplit, slots_per_split, ngroups, n_units;
   float* out;
   float* lse;
   float* part_o;   // [n_rows][nsplit][32][512]
   float* part_ml;  // [n_rows][nsplit][32][2]  (max in log2 domain, sum)
 };
 
+template <int HG>
 struct AttnShared {
   __bf16 kv[kTileTok][kRS];
-  float spart[4][32][kTileTok + 1];
-  __bf16 p_hi[32][kTileTok + 8];
-  __bf16 p_lo[32][kTileTok + 8];
-  float tsc[kTileTok];           // per-token value scale (1 for bf16 rows, 0 if masked)
-  int64_t tlat[kTileTok];        // byte offset of the token's latent row in the pool, -1 masked
-  int64_t trope[kTileTok];
-  float m_run[32], l_run[32], alpha[32];
-  uint16_t lut[256];             // e4m3 -> bf16 bits
+  float spart[HG == 32 ? 4 : 2][HG][kTileTok + 1];
+  __bf16 p_hi[HG][kTileTok + 8];
+  __bf16 p_lo[HG][kTileTok + 8];
+  float tsc[kTileTok];         // per-token value scale of the current tile (fp8)
+  int32_t tt[kMaxWgTok];       // token table: page * 512 + slot, or kMasked / kUnreadable
+  float m_run[HG], l_run[HG], alpha[HG];
+  uint16_t lut[256];           // e4m3 -> bf16 bits
+  int32_t bad;                 // a selected token the table could not name
 };
 
 __device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
@@ -83,288 +93,689 @@ __device__ __forceinline__ float bf16_to_f(__bf16 x) {
   return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, x)) << 16);
 }
 
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA B fragment of 8 consecutive rows (K) of one column (N) from a row-major
+// bf16 LDS tile, with two transpose reads (ds_read_b64_tr_b16). Within a 16-lane
+// group, lane i receives, as element k, element i % 4 of the 8 bytes that lane
+// 4k + i / 4 of the group addresses; so lane j of the group addresses row
+// k0 + j / 4 (+ 4 for the second read), columns n0 + 4 (j % 4) .. + 3, and lane i
+// ends up with rows k0 .. k0 + 7 of column n0 + i.
+__device__ __forceinline__ bf16x8 bfrag_tr(const __bf16* tile, int stride, int k0, int n0, int j) {
+  const __bf16* p = tile + (k0 + (j >> 2)) * stride + n0 + 4 * (j & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * stride));
+  const short __attribute__((ext_vector_type(8))) v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Reductions over groups of 8 or 16 consecutive lanes with DPP (no LDS round trip).
+template <int ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  x = __builtin_fmaxf(x, dpp<kQuadXor1>(x));
+  x = __builtin_fmaxf(x, dpp<kQuadXor2>(x));
+  x = __builtin_fmaxf(x, dpp<kHalfMirror>(x));
+  if (N == 16) x = __builtin_fmaxf(x, dpp<kRowMirror>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kHalfMirror>(x);
+  if (N == 16) x += dpp<kRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ int64_t row_base(const AttnArgs& a, int32_t tt) {
+  return (int64_t)(tt >> 9) * a.v.page_bytes + a.v.cache_off;
+}
+
+// Pieces of one tile a thread loads: bf16 rows are 64 latent + 8 rope 16-byte
+// pieces per token (9 per thread); fp8 rows 32 + 8 (5 per thread).
 template <bool FP8>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
-  __shared__ AttnShared sh;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, n = lane & 31;
-  const int r = blockIdx.y, split = blockIdx.x;
-  const int b = a.row_stream[r];
-  const int t = a.row_pos[r];
-  const int j0 = split * a.slots_per_split;
-  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+struct Gather {
+  static constexpr int kPieces = FP8 ? 40 : 72;
+  static constexpr int kLatPieces = FP8 ? 32 : 64;
+  static constexpr int kPerThread = kTileTok * kPieces / 256;
+  uint4 v[kPerThread];
+  float sc;  // this thread's token scale (threads < 32, fp8)
 
-  if (FP8) sh.lut[tid] = e4m3_to_bf16_bits((uint32_t)tid);
-  if (tid < 32) {
-    sh.m_run[tid] = -__builtin_inff();
-    sh.l_run[tid] = 0.f;
-  }
-
-  // Query fragments of this wave's k-steps: latent steps 8w..8w+7, rope step 32+w.
-  bf16x8 aq[9];
-  {
-    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + n) * kRow + g * 8;
+  __device__ __forceinline__ void issue(const AttnArgs& a, const int32_t* tt, int tok0, int tid) {
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      const int ks = i < 8 ? wave * 8 + i : 32 + wave;
-      aq[i] = n < a.n_heads ? *(const bf16x8*)(qr + ks * 16) : bf16x8{};
+    for (int i = 0; i < kPerThread; ++i) {
+      const int u = tid + i * 256;
+      const int tok = u / kPieces, pc = u % kPieces;
+      const int32_t e = tt[tok0 + tok];
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (e >= 0) {
+        const int64_t base = row_base(a, e);
+        const int slot = e & 511;
+        const char* src = pc < kLatPieces
+                              ? a.v.pool + base + (int64_t)slot * a.lat_row_bytes + pc * 16
+                              : a.v.pool + base + a.off_rope + (int64_t)slot * (kRope * 2) + (pc - kLatPieces) * 16;
+        v[i] = *(const uint4*)src;
+      }
+    }
+    if (FP8 && tid < kTileTok) {
+      const int32_t e = tt[tok0 + tid];
+      sc = 0.f;
+      if (e >= 0) sc = *(const float*)(a.v.pool + row_base(a, e) + a.off_scale + 4LL * (e & 511));
     }
   }
-  f32x16 o[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x16{};
 
-  for (int j = j0; j < j1; j += 8) {
-    // ---- token table of the tile ------------------------------------------------
+  template <int HG>
+  __device__ __forceinline__ void store(AttnShared<HG>& sh, const int32_t* tt, int tok0, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int u = tid + i * 256;
+      const int tok = u / kPieces, pc = u % kPieces;
+      if (!FP8) {
+        *(uint4*)&sh.kv[tok][pc < 64 ? pc * 8 : kLatent + (pc - 64) * 8] = v[i];
+      } else if (pc < 32) {
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t o8[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = w4[j];
+          o8[2 * j] = (uint32_t)sh.lut[x & 255u] | ((uint32_t)sh.lut[(x >> 8) & 255u] << 16);
+          o8[2 * j + 1] = (uint32_t)sh.lut[(x >> 16) & 255u] | ((uint32_t)sh.lut[x >> 24] << 16);
+        }
+        *(uint4*)&sh.kv[tok][pc * 16] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+        *(uint4*)&sh.kv[tok][pc * 16 + 8] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+      } else {
+        *(uint4*)&sh.kv[tok][kLatent + (pc - 32) * 8] = v[i];
+      }
+    }
     if (tid < kTileTok) {
-      const int slot = j + tid / 4;
-      const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
-      const int s = blk * kPoolRatio + (tid & 3);
-      int64_t lat = -1, rope = -1;
-      float sc = 0.f;
-      if (blk >= 0 && s <= t) {
-        const int page = page_of(a.v, b, s / kPageRows);
-        if (page >= 0) {
-          const int64_t base = (int64_t)page * a.v.page_bytes + a.v.cache_off;
-          const int slot_in = s % kPageRows;
-          lat = base + (int64_t)slot_in * a.lat_row_bytes;
-          rope = base + a.off_rope + (int64_t)slot_in * (kRope * 2);
-          sc = FP8 ? *(const float*)(a.v.pool + base + a.off_scale + 4LL * slot_in) : 1.f;
-        } else {
-          sc = __builtin_nanf("");  // a selected token the table cannot name
-        }
-      }
-      sh.tlat[tid] = lat;
-      sh.trope[tid] = rope;
-      sh.tsc[tid] = sc;
+      const int32_t e = tt[tok0 + tid];
+      sh.tsc[tid] = FP8 && e >= 0 ? sc : (e >= 0 ? 1.f : 0.f);
     }
-    __syncthreads();
-    // ---- gather: 16-byte pieces, consecutive threads along a row ------------------
-    if (!FP8) {
-      // 64 latent pieces + 8 rope pieces per token
-      for (int u = tid; u < kTileTok * 72; u += 256) {
-        const int tok = u / 72, pc = u % 72;
-        const int64_t base = pc < 64 ? sh.tlat[tok] : sh.trope[tok];
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (base >= 0) val = *(const uint4*)(a.v.pool + base + (pc < 64 ? pc : pc - 64) * 16);
-        *(uint4*)&sh.kv[tok][pc < 64 ? pc * 8 : kLatent + (pc - 64) * 8] = val;
-      }
-    } else {
-      // 32 latent pieces of 16 e4m3 bytes + 8 rope pieces per token
-      for (int u = tid; u < kTileTok * 40; u += 256) {
-        const int tok = u / 40, pc = u % 40;
-        if (pc < 32) {
-          const int64_t base = sh.tlat[tok];
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (base >= 0) val = *(const uint4*)(a.v.pool + base + pc * 16);
-          const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-          uint32_t outw[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t x = w4[i];
-            outw[2 * i] = (uint32_t)sh.lut[x & 255u] | ((uint32_t)sh.lut[(x >> 8) & 255u] << 16);
-            outw[2 * i + 1] = (uint32_t)sh.lut[(x >> 16) & 255u] | ((uint32_t)sh.lut[x >> 24] << 16);
-          }
-          *(uint4*)&sh.kv[tok][pc * 16] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-          *(uint4*)&sh.kv[tok][pc * 16 + 8] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
-        } else {
-          const int64_t base = sh.trope[tok];
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (base >= 0) val = *(const uint4*)(a.v.pool + base + (pc - 32) * 16);
-          *(uint4*)&sh.kv[tok][kLatent + (pc - 32) * 8] = val;
-        }
-      }
-    }
-    __syncthreads();
-    // ---- S partials: this wave's 9 k-steps --------------------------------------
-    {
-      f32x16 accl = {}, accr = {};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ks = wave * 8 + i;
-        const bf16x8 bk = *(const bf16x8*)&sh.kv[n][ks * 16 + g * 8];
-        accl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], bk, accl, 0, 0, 0);
-      }
-      {
-        const bf16x8 bk = *(const bf16x8*)&sh.kv[n][(32 + wave) * 16 + g * 8];
-        accr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[8], bk, accr, 0, 0, 0);
-      }
-      const float tsc = FP8 ? sh.tsc[n] : 1.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * g + (i & 3);
-        sh.spart[wave][m][n] = accl[i] * tsc + accr[i];
-      }
-    }
-    __syncthreads();
-    // ---- online softmax: 8 threads per head, 4 tokens each ----------------------
-    {
-      const int h = tid >> 3, p = tid & 7;
-      float z[4];
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 4 * p + e;
-        const float sc = sh.tsc[tok];
-        float v = (sh.spart[0][h][tok] + sh.spart[1][h][tok] + sh.spart[2][h][tok] + sh.spart[3][h][tok]) *
-                  a.scale_log2;
-        if (sh.tlat[tok] < 0) v = sc != sc ? sc : -__builtin_inff();  // masked (NaN if unreadable)
-        z[e] = v;
-        tmax = __builtin_fmaxf(tmax, v);
-        if (v != v) tmax = v;
-      }
-#pragma unroll
-      for (int o2 = 1; o2 < 8; o2 <<= 1) {
-        const float y = __shfl_xor(tmax, o2, 64);
-        tmax = (y != y) ? y : __builtin_fmaxf(tmax, y);
-      }
-      const float m_old = sh.m_run[h];
-      const float m_new = __builtin_fmaxf(m_old, tmax) + (tmax != tmax ? tmax : 0.f);
-      const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_old - m_new);
-      float lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 4 * p + e;
-        const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
-        lsum += pe;
-        const float pv = FP8 ? pe * sh.tsc[tok] : pe;
-        const __bf16 hi = bf16_rne(pv);
-        sh.p_hi[h][tok] = hi;
-        sh.p_lo[h][tok] = bf16_rne(pv - bf16_to_f(hi));
-      }
-#pragma unroll
-      for (int o2 = 1; o2 < 8; o2 <<= 1) lsum += __shfl_xor(lsum, o2, 64);
-      __syncthreads();  // every thread of the head has read m_run before it changes
-      if (p == 0) {
-        sh.m_run[h] = m_new;
-        sh.l_run[h] = sh.l_run[h] * alpha + lsum;
-        sh.alpha[h] = alpha;
-      }
-    }
-    __syncthreads();
-    // ---- O = alpha * O + P V: wave owns columns [128w, 128w + 128) ---------------
-    {
-      float al[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) al[i] = sh.alpha[8 * (i >> 2) + 4 * g + (i & 3)];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[nt][i] *= al[i];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 ph = *(const bf16x8*)&sh.p_hi[n][ks * 16 + g * 8];
-        const bf16x8 pl = *(const bf16x8*)&sh.p_lo[n][ks * 16 + g * 8];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int d = wave * 128 + nt * 32 + n;
-          bf16x8 vb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vb[e] = sh.kv[ks * 16 + g * 8 + e][d];
-          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vb, o[nt], 0, 0, 0);
-          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vb, o[nt], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
   }
+};
 
-  // ---- write -----------------------------------------------------------------------
+// MFMA fragment geometry. HG = 32: 32x32x16 (one wave covers 32 tokens, the 36
+// k-steps split 9 per wave). HG = 16: 16x16x32 (a wave covers 16 tokens and half
+// of the 18 k-steps).
+template <int HG>
+struct Frag;
+
+template <>
+struct Frag<32> {
+  static constexpr int kParts = 4;  // partial S tiles summed in softmax
+  typedef f32x16 acc_t;
+  // k-steps of 16 dims; wave w takes latent steps 8w..8w+7 and rope step 32+w
+  __device__ static int ks_dim(int wave, int i, int g) {
+    const int ks = i < 8 ? wave * 8 + i : 32 + wave;
+    return ks * 16 + g * 8;
+  }
+  static constexpr int kSteps = 9;
+  __device__ static int tok_of_lane(int wave, int lane) { return lane & 31; }
+  __device__ static int part_of(int wave) { return wave; }
+  __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static constexpr int kAccN = 16;
+  __device__ static int row_of(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+  // A-operand lane geometry: head = lane % 32, k-slice half = lane / 32
+  __device__ static int a_row(int lane) { return lane & 31; }
+  __device__ static int a_half(int lane) { return lane >> 5; }
+  static constexpr int kNT = 4;        // 32-column tiles per wave in P.V
+  static constexpr int kNTW = 32;
+  static constexpr int kPVsteps = 2;   // 16 tokens per k-step
+  static constexpr int kPVk = 16;
+};
+
+template <>
+struct Frag<16> {
+  static constexpr int kParts = 2;
+  typedef f32x4 acc_t;
+  // k-steps of 32 dims; wave w: token half w%2, latent steps 8(w/2)..+7 and rope step 16 + w/2
+  __device__ static int ks_dim(int wave, int i, int g) {
+    const int ks = i < 8 ? (wave >> 1) * 8 + i : 16 + (wave >> 1);
+    return ks * 32 + g * 8;
+  }
+  static constexpr int kSteps = 9;
+  __device__ static int tok_of_lane(int wave, int lane) { return (wave & 1) * 16 + (lane & 15); }
+  __device__ static int part_of(int wave) { return wave >> 1; }
+  __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static constexpr int kAccN = 4;
+  __device__ static int row_of(int i, int lane) { return 4 * (lane >> 4) + i; }
+  __device__ static int a_row(int lane) { return lane & 15; }
+  __device__ static int a_half(int lane) { return lane >> 4; }
+  static constexpr int kNT = 8;        // 16-column tiles per wave in P.V
+  static constexpr int kNTW = 16;
+  static constexpr int kPVsteps = 1;   // 32 tokens per k-step
+  static constexpr int kPVk = 32;
+};
+
+// Online softmax of one 32-token tile for HG heads: 256 / HG threads per head, the
+// partial S tiles summed, masked tokens at -inf; writes P (hi, lo) and the
+// per-head rescale factor.
+template <int HG, int NPARTS, bool FP8, typename SH>
+__device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const float* tsc, float scale_log2, int tid) {
+  constexpr int TPH = 256 / HG, TPT = kTileTok / TPH;
+  const int h = tid / TPH, p = tid % TPH;
+  float z[TPT];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int e = 0; e < TPT; ++e) {
+    const int tok = p * TPT + e;
+    float v = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NPARTS; ++pp) v += sh.spart[pp][h][tok];
+    v *= scale_log2;
+    if (tt[tok] < 0) v = -__builtin_inff();   // not attended
+    z[e] = v;
+    tmax = __builtin_fmaxf(tmax, v);
+  }
+  tmax = group_max<TPH>(tmax);
+  const float m_old = sh.m_run[h];
+  const float m_new = __builtin_fmaxf(m_old, tmax);
+  const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_old - m_new);
+  float lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < TPT; ++e) {
+    const int tok = p * TPT + e;
+    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
+    lsum += pe;
+    const float pv = FP8 ? pe * tsc[tok] : pe;
+    const __bf16 hi = bf16_rne(pv);
+    sh.p_hi[h][tok] = hi;
+    sh.p_lo[h][tok] = bf16_rne(pv - bf16_to_f(hi));
+  }
+  lsum = group_sum<TPH>(lsum);
+  __syncthreads();  // every thread of the head has read m_run
+  if (p == 0) {
+    sh.m_run[h] = m_new;
+    sh.l_run[h] = sh.l_run[h] * alpha + lsum;
+    sh.alpha[h] = alpha;
+  }
+}
+
+// Final normalization (one split) or the split's partial (O, max, sum).
+template <int HG, typename F, typename SH>
+__device__ __forceinline__ void write_out(const AttnArgs& a, SH& sh, const typename F::acc_t* o, int r, int split,
+                                          int h0, int wave, int lane, int tid) {
+  const int col = F::a_row(lane);
+  const bool bad = sh.bad != 0;   // a selected token the table could not name
+  const float qnan = __builtin_nanf("");
   if (a.nsplit == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * g + (i & 3);
-      if (m >= a.n_heads) continue;
+    for (int i = 0; i < F::kAccN; ++i) {
+      const int m = F::row_of(i, lane);
+      const int head = h0 + m;
+      if (head >= a.n_heads) continue;
       const float l = sh.l_run[m];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float* orow = a.out + ((int64_t)r * a.n_heads + m) * kLatent + wave * 128 + n;
+      float* orow = a.out + ((int64_t)r * a.n_heads + head) * kLatent + wave * 128 + col;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) orow[nt * 32] = o[nt][i] * inv;
+      for (int nt = 0; nt < F::kNT; ++nt) orow[nt * F::kNTW] = bad ? qnan : o[nt][i] * inv;
     }
-    if (a.lse && tid < a.n_heads) {
+    if (a.lse && tid < HG && h0 + tid < a.n_heads) {
       const float l = sh.l_run[tid];
-      a.lse[(int64_t)r * a.n_heads + tid] =
-          l > 0.f ? (sh.m_run[tid] + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+      a.lse[(int64_t)r * a.n_heads + h0 + tid] =
+          bad ? qnan : (l > 0.f ? (sh.m_run[tid] + log2f(l)) * 0.69314718055994531f : -__builtin_inff());
     }
   } else {
     float* po = a.part_o + ((int64_t)r * a.nsplit + split) * 32 * kLatent;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * g + (i & 3);
-      float* orow = po + (int64_t)m * kLatent + wave * 128 + n;
+    for (int i = 0; i < F::kAccN; ++i) {
+      const int m = F::row_of(i, lane);
+      float* orow = po + (int64_t)(h0 + m) * kLatent + wave * 128 + col;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) orow[nt * 32] = o[nt][i];
+      for (int nt = 0; nt < F::kNT; ++nt) orow[nt * F::kNTW] = o[nt][i];
     }
-    if (tid < 32) {
-      float* pm = a.part_ml + (((int64_t)r * a.nsplit + split) * 32 + tid) * 2;
+    if (tid < HG) {
+      float* pm = a.part_ml + (((int64_t)r * a.nsplit + split) * 32 + h0 + tid) * 2;
       pm[0] = sh.m_run[tid];
-      pm[1] = sh.l_run[tid];
+      pm[1] = bad ? qnan : sh.l_run[tid];
     }
   }
 }
 
-// Combine the splits of one (row, head): 128 threads x 4 columns.
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+template <int HG, bool FP8>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+  typedef Frag<HG> F;
+  __shared__ AttnShared<HG> sh;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+
+  // ---- which (row, head group, split) ------------------------------------------
+  int unit, hg;
+  if (a.ngroups == 1) {
+    unit = blockIdx.x;
+    hg = 0;
+  } else {  // the two head groups of a unit are 8 workgroups apart: same XCD
+    unit = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    hg = (blockIdx.x >> 3) & 1;
+  }
+  if (unit >= a.n_units) return;
+  const int r = unit % a.n_rows, split = unit / a.n_rows;
+  const int h0 = hg * HG;
+  const int b = a.row_stream[r];
+  const int t = a.row_pos[r];
+  const int j0 = split * a.slots_per_split;
+  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
+  const int ntiles = (ntok + kTileTok - 1) / kTileTok;
+
+  if (FP8) sh.lut[tid] = e4m3_to_bf16_bits((uint32_t)tid);
+  if (tid < HG) {
+    sh.m_run[tid] = -__builtin_inff();
+    sh.l_run[tid] = 0.f;
+  }
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();
+  // ---- token table ----------------------------------------------------------------
+  for (int i = tid; i < ntiles * kTileTok; i += 256) {
+    const int slot = j0 + i / kPoolRatio;
+    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
+    const int s = blk * kPoolRatio + (i & 3);
+    int32_t e = kMasked;
+    if (blk >= 0 && s <= t) {
+      const int page = page_of(a.v, b, s / kPageRows);
+      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
+      if (page < 0) sh.bad = 1;
+    }
+    sh.tt[i] = e;
+  }
+  // ---- query fragments --------------------------------------------------------------
+  bf16x8 aq[F::kSteps];
+  {
+    const int head = h0 + F::a_row(lane);
+    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + head) * kRow;
+#pragma unroll
+    for (int i = 0; i < F::kSteps; ++i)
+      aq[i] = head < a.n_heads ? *(const bf16x8*)(qr + F::ks_dim(wave, i, F::a_half(lane))) : bf16x8{};
+  }
+  typename F::acc_t o[F::kNT];
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt) o[nt] = typename F::acc_t{};
+  __syncthreads();
+
+  Gather<FP8> gat;
+  if (ntiles > 0) gat.issue(a, sh.tt, 0, tid);
+  for (int it = 0; it < ntiles; ++it) {
+    gat.store(sh, sh.tt, it * kTileTok, tid);
+    if (it + 1 < ntiles) gat.issue(a, sh.tt, (it + 1) * kTileTok, tid);
+    __syncthreads();
+    // ---- S partials ---------------------------------------------------------------
+    {
+      typename F::acc_t accl{}, accr{};
+      const int tok = F::tok_of_lane(wave, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 bk = *(const bf16x8*)&sh.kv[tok][F::ks_dim(wave, i, F::a_half(lane))];
+        accl = F::mfma(aq[i], bk, accl);
+      }
+      {
+        const bf16x8 bk = *(const bf16x8*)&sh.kv[tok][F::ks_dim(wave, 8, F::a_half(lane))];
+        accr = F::mfma(aq[8], bk, accr);
+      }
+      const float tsc = FP8 ? sh.tsc[tok] : 1.f;
+#pragma unroll
+      for (int i = 0; i < F::kAccN; ++i) sh.spart[F::part_of(wave)][F::row_of(i, lane)][tok] = accl[i] * tsc + accr[i];
+    }
+    __syncthreads();
+    softmax_tile<HG, F::kParts, FP8>(sh, sh.tt + it * kTileTok, sh.tsc, a.scale_log2, tid);
+    __syncthreads();
+    // ---- O = alpha O + P V ------------------------------------------------------------
+    {
+      float al[F::kAccN];
+#pragma unroll
+      for (int i = 0; i < F::kAccN; ++i) al[i] = sh.alpha[F::row_of(i, lane)];
+#pragma unroll
+      for (int nt = 0; nt < F::kNT; ++nt)
+#pragma unroll
+        for (int i = 0; i < F::kAccN; ++i) o[nt][i] *= al[i];
+      const int arow = F::a_row(lane), ahalf = F::a_half(lane);
+      const int grp = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int ks = 0; ks < F::kPVsteps; ++ks) {
+        const int tk = ks * F::kPVk + ahalf * 8;
+        const bf16x8 ph = *(const bf16x8*)&sh.p_hi[arow][tk];
+        const bf16x8 pl = *(const bf16x8*)&sh.p_lo[arow][tk];
+#pragma unroll
+        for (int nt = 0; nt < F::kNT; ++nt) {
+          // this 16-lane group's 8 tokens and 16 columns of the B fragment
+          const int k0 = ks * F::kPVk + (HG == 32 ? (grp >> 1) * 8 : grp * 8);
+          const int n0 = wave * 128 + nt * F::kNTW + (HG == 32 ? (grp & 1) * 16 : 0);
+          const bf16x8 vb = bfrag_tr(&sh.kv[0][0], kRS, k0, n0, j);
+          o[nt] = F::mfma(ph, vb, o[nt]);
+          o[nt] = F::mfma(pl, vb, o[nt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  write_out<HG, F>(a, sh, o, r, split, h0, wave, lane, tid);
+}
+
+// ---- decode: every row of the workgroup in LDS at once ------------------------------------
+// Few rows (decode): a workgroup owns 16 heads and at most 128 tokens of one row.
+// All of its latent rows go global -> LDS directly (one 1 KiB wave-wide load per
+// token, no registers) and its rope rows eight tokens per load, so every byte the
+// workgroup needs is in flight at once. Then one pass: S for all 128 tokens (wave w
+// takes tokens 32w..32w+31 with four independent MFMA chains), one softmax per head
+// (no running rescale), and O = P V with K = 128. bf16 rows only.
+constexpr int kDecTok = 128;
+constexpr int kDecRS = kLatent + 16;   // bf16 per LDS latent row (1,056 bytes: conflict-free transposes)
+constexpr int kDecSS = kDecTok + 4;    // fp32 per S row
+constexpr int kDecPS = kDecTok + 8;    // bf16 per P row
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct DecShared {
+  __bf16 lat[kDecTok][kDecRS];
+  __bf16 rope[kDecTok][kRope];
+  union {                        // S, then (after every thread has read its S) P as hi + lo
+    float s[16][kDecSS];
+    struct {
+      __bf16 hi[16][kDecPS];
+      __bf16 lo[16][kDecPS];
+    } p;
+  } sp;
+  int32_t tt[kDecTok];
+  int64_t tlat[kDecTok];         // byte offset of the token's latent row, -1 when not attended
+  float m_run[16], l_run[16];
+  int32_t bad;
+};
+
+__global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
+  typedef Frag<16> F;
+  __shared__ DecShared sh;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  int unit, hg;
+  if (a.ngroups == 1) {
+    unit = blockIdx.x;
+    hg = 0;
+  } else {
+    unit = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    hg = (blockIdx.x >> 3) & 1;
+  }
+  if (unit >= a.n_units) return;
+  const int r = unit % a.n_rows, split = unit / a.n_rows;
+  const int h0 = hg * 16;
+  const int b = a.row_stream[r];
+  const int t = a.row_pos[r];
+  const int j0 = split * a.slots_per_split;
+  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
+  const int ntiles = (ntok + kTileTok - 1) / kTileTok;   // <= 4
+  const int nt32 = ntiles * kTileTok;
+
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();
+  if (tid < kDecTok) {
+    const int slot = j0 + tid / kPoolRatio;
+    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
+    const int s = blk * kPoolRatio + (tid & 3);
+    int32_t e = kMasked;
+    int64_t off = -1;
+    if (blk >= 0 && s <= t) {
+      const int page = page_of(a.v, b, s / kPageRows);
+      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
+      if (page >= 0) off = row_base(a, e) + (int64_t)(e & 511) * a.lat_row_bytes;
+      else sh.bad = 1;
+    }
+    sh.tt[tid] = e;
+    sh.tlat[tid] = off;
+  }
+  // query fragments: all 18 k-steps (32 dims each) of this lane's head
+  bf16x8 aq[18];
+  {
+    const int head = h0 + (lane & 15);
+    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + head) * kRow + (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) aq[ks] = head < a.n_heads ? *(const bf16x8*)(qr + ks * 32) : bf16x8{};
+  }
+  __syncthreads();
+  // ---- every load of the workgroup at once -----------------------------------------
+  // wave w owns tokens w, w + 4, ... (lane i: token w + 4i); rope groups of 8 tokens
+  // w, w + 4, ... (lane l: token 8g + l/8, piece l%8). Offsets are read before any
+  // load is issued, so no wait falls between the loads.
+  const int my_n = (nt32 - wave + 3) / 4;
+  const int64_t my_off = lane < my_n ? sh.tlat[wave + 4 * lane] : -1;
+  const char* rsrc[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int g8 = wave + 4 * q4;
+    const int tok = g8 * 8 + (lane >> 3);
+    const int32_t e = tok < nt32 ? sh.tt[tok] : kMasked;
+    rsrc[q4] = e >= 0 ? a.v.pool + row_base(a, e) + a.off_rope + (int64_t)(e & 511) * (kRope * 2) + (lane & 7) * 16
+                      : a.v.pool + (lane & 7) * 16;   // any readable bytes: masked tokens never reach P V
+  }
+  uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)(my_off >> 32);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < my_n) {
+      const uint32_t lo = __builtin_amdgcn_readlane(off_lo, i);
+      const uint32_t hi = __builtin_amdgcn_readlane(off_hi, i);
+      const int64_t off = (int64_t)(((uint64_t)hi << 32) | lo);
+      if (off >= 0)
+        __builtin_amdgcn_global_load_lds((const void*)(a.v.pool + off + lane * 16),
+                                         (lds_void*)&sh.lat[wave + 4 * i][0], 16, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int g8 = wave + 4 * q4;
+    if (g8 * 8 < nt32) __builtin_amdgcn_global_load_lds((const void*)rsrc[q4], (lds_void*)&sh.rope[g8 * 8][0], 16, 0, 0);
+  }
+  // rows not attended are zero (P V multiplies them by 0)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < my_n && (int32_t)__builtin_amdgcn_readlane(off_hi, i) < 0)
+      *(uint4*)&sh.lat[wave + 4 * i][lane * 8] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  // ---- S for tokens 32w .. 32w + 31: two 16-token N tiles x two k halves ------------
+  if (wave < ntiles) {
+    f32x4 acc[2][2] = {};
+    const int tok0 = wave * kTileTok + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+      for (int n2 = 0; n2 < 2; ++n2) {
+        const int tok = tok0 + 16 * n2;
+        const int d = ks * 32 + (lane >> 4) * 8;
+        const bf16x8 bk = ks < 16 ? *(const bf16x8*)&sh.lat[tok][d] : *(const bf16x8*)&sh.rope[tok][d - kLatent];
+        acc[n2][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], bk, acc[n2][ks & 1], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sh.sp.s[4 * (lane >> 4) + i][wave * kTileTok + 16 * n2 + (lane & 15)] =
+            (acc[n2][0][i] + acc[n2][1][i]) * a.scale_log2;
+  }
+  __syncthreads();
+  // ---- softmax: 16 threads per head, 8 tokens each ----------------------------------
+  {
+    const int h = tid >> 4, p = tid & 15;
+    float z[8];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = p * 8 + e;
+      const float v = tok < nt32 && sh.tt[tok] >= 0 ? sh.sp.s[h][tok] : -__builtin_inff();
+      z[e] = v;
+      mx = __builtin_fmaxf(mx, v);
+    }
+    mx = group_max<16>(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      z[e] = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - mx);
+      sum += z[e];
+    }
+    sum = group_sum<16>(sum);
+    __syncthreads();   // S is read by every thread before P overwrites it
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 hi = bf16_rne(z[e]);
+      sh.sp.p.hi[h][p * 8 + e] = hi;
+      sh.sp.p.lo[h][p * 8 + e] = bf16_rne(z[e] - bf16_to_f(hi));
+    }
+    if (p == 0) {
+      sh.m_run[h] = mx;
+      sh.l_run[h] = sum;
+    }
+  }
+  __syncthreads();
+  // ---- O = P V: wave w owns columns 128w .. 128w + 127 (8 tiles of 16) ---------------
+  F::acc_t o[F::kNT];
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt) o[nt] = F::acc_t{};
+  {
+    const int arow = lane & 15, grp = lane >> 4, j = lane & 15;
+    for (int ks = 0; ks < ntiles; ++ks) {
+      const bf16x8 ph = *(const bf16x8*)&sh.sp.p.hi[arow][ks * 32 + grp * 8];
+      const bf16x8 pl = *(const bf16x8*)&sh.sp.p.lo[arow][ks * 32 + grp * 8];
+#pragma unroll
+      for (int nt = 0; nt < F::kNT; ++nt) {
+        const bf16x8 vb = bfrag_tr(&sh.lat[0][0], kDecRS, ks * 32 + grp * 8, wave * 128 + nt * 16, j);
+        o[nt] = F::mfma(ph, vb, o[nt]);
+        o[nt] = F::mfma(pl, vb, o[nt]);
+      }
+    }
+  }
+  write_out<16, F>(a, sh, o, r, split, h0, wave, lane, tid);
+}
+
+// Combine the splits of one (row, head): 256 threads x 2 columns, weights in LDS.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float wgt[64];
+  __shared__ float tot[2];
   const int r = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
   const float* pml = a.part_ml + (int64_t)r * a.nsplit * 64;
-  float M = -__builtin_inff();
-  bool nan = false;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float m = pml[(s * 32 + h) * 2], l = pml[(s * 32 + h) * 2 + 1];
-    if (m != m || l != l) nan = true;
-    if (l > 0.f) M = __builtin_fmaxf(M, m);
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    float m = -__builtin_inff(), l = 0.f;
+    if (s < a.nsplit) {
+      m = pml[(s * 32 + h) * 2];
+      l = pml[(s * 32 + h) * 2 + 1];
+    }
+    bool nan = (m != m) || (l != l);
+    float M = l > 0.f ? m : -__builtin_inff();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      M = __builtin_fmaxf(M, __shfl_xor(M, o, 64));
+      nan |= __shfl_xor((int)nan, o, 64) != 0;
+    }
+    const float f = l > 0.f ? exp2f(m - M) : 0.f;
+    float L = l * f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o, 64);
+    wgt[s] = f;
+    if (s == 0) {
+      tot[0] = nan ? __builtin_nanf("") : L;
+      tot[1] = M;
+    }
   }
-  float L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int d = threadIdx.x * 4;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float m = pml[(s * 32 + h) * 2], l = pml[(s * 32 + h) * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float f = exp2f(m - M);
-    L += l * f;
-    const float4 v = *(const float4*)(a.part_o + (((int64_t)r * a.nsplit + s) * 32 + h) * kLatent + d);
-    acc.x += v.x * f;
-    acc.y += v.y * f;
-    acc.z += v.z * f;
-    acc.w += v.w * f;
+  __syncthreads();
+  const float L = tot[0];
+  const int d = threadIdx.x * 2;
+  const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + d;
+  float2 acc = make_float2(0.f, 0.f);
+  int s = 0;
+  for (; s + 8 <= a.nsplit; s += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const float2*)(po + (int64_t)(s + u) * 32 * kLatent);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = wgt[s + u];
+      if (f != 0.f) {
+        acc.x += v[u].x * f;
+        acc.y += v[u].y * f;
+      }
+    }
+  }
+  for (; s < a.nsplit; ++s) {
+    const float f = wgt[s];
+    if (f != 0.f) {
+      const float2 v = *(const float2*)(po + (int64_t)s * 32 * kLatent);
+      acc.x += v.x * f;
+      acc.y += v.y * f;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float4 res = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (nan) res = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
-  *(float4*)(a.out + ((int64_t)r * a.n_heads + h) * kLatent + d) = res;
+  float2 res = make_float2(acc.x * inv, acc.y * inv);
+  if (L != L) res = make_float2(L, L);
+  *(float2*)(a.out + ((int64_t)r * a.n_heads + h) * kLatent + d) = res;
   if (a.lse && threadIdx.x == 0)
     a.lse[(int64_t)r * a.n_heads + h] =
-        nan ? __builtin_nanf("") : (L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff());
+        L != L ? L : (L > 0.f ? (tot[1] + log2f(L)) * 0.69314718055994531f : -__builtin_inff());
 }
 
-static void pick_split(int32_t n_rows, int32_t k, int& nsplit, int& sps) {
+struct SplitPlan {
+  int nsplit, sps, ngroups, hg, n_units, grid;
+  bool decode;  // all tiles in LDS at once (bf16, <= 128 tokens per workgroup)
+};
+
+// Few rows (decode): 16 heads and at most 128 tokens per workgroup, so a row is
+// spread over many CUs. Many rows (prefill): all 32 heads and the whole block list
+// (up to 2,048 tokens) per workgroup.
+static SplitPlan pick_split(int32_t n_rows, int32_t n_heads, int32_t k, bool fp8) {
+  SplitPlan p;
   const int tiles = (k + 7) / 8;
-  int s = (256 + n_rows - 1) / n_rows;
-  if (s > tiles) s = tiles;
-  if (s < 1) s = 1;
-  const int tiles_per = (tiles + s - 1) / s;
-  sps = tiles_per * 8;
-  nsplit = (k + sps - 1) / sps;
+  p.hg = (n_heads <= 16 || n_rows < 128) ? 16 : 32;
+  p.ngroups = (n_heads + p.hg - 1) / p.hg;
+  p.decode = p.hg == 16 && !fp8 && n_rows < 128;
+  int tiles_per;
+  if (p.decode) {
+    tiles_per = kDecTok / kTileTok;
+  } else {
+    int s = (256 + n_rows * p.ngroups - 1) / (n_rows * p.ngroups);
+    if (s > tiles) s = tiles;
+    if (s > 64) s = 64;
+    if (s < 1) s = 1;
+    tiles_per = (tiles + s - 1) / s;
+    if (tiles_per * kTileTok > kMaxWgTok) tiles_per = kMaxWgTok / kTileTok;
+  }
+  if (tiles_per > tiles) tiles_per = tiles;
+  p.sps = tiles_per * 8;
+  p.nsplit = (k + p.sps - 1) / p.sps;
+  p.n_units = n_rows * p.nsplit;
+  p.grid = p.ngroups == 1 ? p.n_units : ((p.n_units + 7) / 8) * 16;
+  return p;
 }
 
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {
-  (void)n_heads;
-  int ns, sps;
-  pick_split(n_rows, k, ns, sps);
-  if (ns == 1) return 0;
-  return (size_t)n_rows * ns * 32 * (kLatent + 2) * sizeof(float);
+  // the larger of the two formats' needs (the format is not an argument here)
+  SplitPlan p = pick_split(n_rows, n_heads, k, false);
+  const SplitPlan q = pick_split(n_rows, n_heads, k, true);
+  if (q.nsplit > p.nsplit) p = q;
+  if (p.nsplit == 1) return 0;
+  return (size_t)n_rows * p.nsplit * 32 * (kLatent + 2) * sizeof(float);
 }
 
-tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const int32_t* row_stream,
                       const int32_t* row_pos, const void* q, int32_t n_heads, float scale,
                       const int32_t* blocks, int32_t k, float* out, float* lse, void* ws,
                       size_t ws_bytes, hipStream_t st) {
   (void)ws_bytes;
   AttnArgs a;
   a.v = v;
-  a.off_scale = p->off_scale;
-  a.off_rope = p->off_rope;
-  a.lat_row_bytes = (int32_t)p->lat_row_bytes;
+  a.off_scale = pl->off_scale;
+  a.off_rope = pl->off_rope;
+  a.lat_row_bytes = (int32_t)pl->lat_row_bytes;
   a.n_rows = n_rows;
   a.row_stream = row_stream;
   a.row_pos = row_pos;
@@ -373,21 +784,28 @@ tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const 
   a.scale_log2 = scale * 1.4426950408889634f;
   a.blocks = blocks;
   a.k = k;
-  int ns, sps;
-  pick_split(n_rows, k, ns, sps);
-  a.nsplit = ns;
-  a.slots_per_split = sps;
+  const bool fp8 = pl->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE;
+  const SplitPlan p = pick_split(n_rows, n_heads, k, fp8);
+  a.nsplit = p.nsplit;
+  a.slots_per_split = p.sps;
+  a.ngroups = p.ngroups;
+  a.n_units = p.n_units;
   a.out = out;
   a.lse = lse;
-  a.part_o = ns > 1 ? (float*)ws : nullptr;
-  a.part_ml = ns > 1 ? (float*)ws + (size_t)n_rows * ns * 32 * kLatent : nullptr;
-  if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_sparse_mla_attn: at most 65535 rows per call");
-  const bool fp8 = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE;
-  if (fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(ns, n_rows), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_kernel<false>, dim3(ns, n_rows), dim3(256), 0, st, a);
+  a.part_o = p.nsplit > 1 ? (float*)ws : nullptr;
+  a.part_ml = p.nsplit > 1 ? (float*)ws + (size_t)n_rows * p.nsplit * 32 * kLatent : nullptr;
+  if (p.decode) {
+    hipLaunchKernelGGL(attn_decode_kernel, dim3(p.grid), dim3(256), 0, st, a);
+  } else if (p.hg == 16) {
+    if (fp8) hipLaunchKernelGGL((attn_kernel<16, true>), dim3(p.grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<16, false>), dim3(p.grid), dim3(256), 0, st, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((attn_kernel<32, true>), dim3(p.grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<32, false>), dim3(p.grid), dim3(256), 0, st, a);
+  }
   tf_status s = launch_status("tf_sparse_mla_attn");
-  if (s != TF_OK || ns == 1) return s;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(128), 0, st, a);
+  if (s != TF_OK || p.nsplit == 1) return s;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(256), 0, st, a);
   return launch_status("tf_sparse_mla_attn");
 }
 

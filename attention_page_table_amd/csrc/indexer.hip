@@ -5,15 +5,22 @@
 // [#1142, "GLM declares a kv_pool.Layout"]: the pooled keys are read through the
 // page table.
 //
-// Design (gfx950): one v_mfma_f32_32x32x16_bf16 tile is 32 (row, head) pairs x
-// 32 keys x 16 dims. The 32 A-rows are 32/H query rows of H heads each, arranged
-// so that each lane's 16 accumulators are all H heads of 16/H rows for one key;
-// the ReLU, the weights and the head sum then stay inside the lane (no shuffles),
-// and each half-wave stores 32 consecutive keys of a row (128-byte stores).
-// Queries stay in registers for the whole launch; keys stream through once per
-// row tile, loaded straight from the page into MFMA B fragments. The rows of one
-// tile share B only when their tables name the same page for the key tile (one
-// stream, or shared prefix pages); otherwise each distinct page is a pass of its own.
+// One v_mfma_f32_32x32x16_bf16 tile is 32 (row, head) pairs x 32 keys x 16 dims.
+// Its 32 A-rows are arranged so that each lane's 16 accumulators are all the heads
+// of the rows its half-wave holds, for one key: the ReLU, the weights and the head
+// sum stay inside the lane (no shuffles) and each half-wave stores 32 consecutive
+// keys of a row (128-byte stores).
+//
+// Two kernels:
+//  * tile kernel (many rows of one stream, e.g. a prefill chunk; MFMA-bound): a
+//    workgroup holds the queries of 4 x MT x (32/H) rows in registers and streams a
+//    key range through LDS in 32-key subtiles (double-buffered global -> LDS loads,
+//    16-byte chunks XOR-swizzled so the B-fragment reads are conflict-free); each
+//    B fragment read from LDS feeds MT tiles. Workgroups whose rows are not all of
+//    one stream take the per-row path.
+//  * row kernel (few rows of distinct streams, e.g. a decode batch; HBM-bound): each
+//    wave streams one row's keys straight into B fragments, one subtile ahead, with
+//    the row's page ids preloaded across the lanes.
 #include "common.h"
 
 namespace tf {
@@ -30,19 +37,165 @@ struct IdxArgs {
   float* logits;
   int64_t ld;
   int32_t* n_valid;
-  int32_t keys_per_wg;
+  int32_t keys_per_wg;   // multiple of 128
+  int32_t n_kgroups;
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
+  const int pos = a.row_pos[row];
+  if (pos < 0) return 0;
+  const int64_t nc = (int64_t)pos / kPoolRatio + 1;
+  return (int)(nc < a.ld ? nc : a.ld);
+}
+
+// ---- per-row path: one wave streams one row over keys [kb, ke) ---------------------------
+// A-rows with bit 2 clear carry the row's heads (head 4 * (m / 8) + m % 4), the others are
+// zero; lanes 0..31 then hold every head of key n = lane in accumulators 0..H-1.
+template <int H, int D>
+__device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke, int lane) {
+  constexpr int KS = D / 16;
+  const int g = lane >> 5, n = lane & 31;
+  const int b = a.row_stream[row];
+  const int nc = nc_of(a, row);
+  const float ninf = -__builtin_inff();
+  float* out = a.logits + (int64_t)row * a.ld;
+  bf16x8 aq[KS];
+  {
+    const int m = n;
+    const int u = 4 * (m >> 3) + (m & 3);
+    const bool live = ((m >> 2) & 1) == 0 && u < H;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      aq[ks] = live ? *(const bf16x8*)(a.q + ((int64_t)row * H + u) * D + ks * 16 + g * 8) : bf16x8{};
+  }
+  float wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wv[i] = i < H ? a.w[(int64_t)row * H + i] : 0.f;
+  const int64_t kend = ke < nc ? ke : nc;   // keys that need scores
+  // page ids of the range, one per lane (lane i: page index kb/128 + i)
+  const int p0 = (int)(kb / kKeysPerPage);
+  const int my_page = page_of(a.v, b, p0 + lane);
+  auto page_at = [&](int64_t kt) { return __builtin_amdgcn_readlane(my_page, (int)(kt / kKeysPerPage) - p0); };
+  auto load = [&](int64_t kt, bf16x8 (&bf)[KS]) {
+    const int pg = page_at(kt);
+    if (pg >= 0) {
+      const char* kp = cache_block(a.v, pg) + a.off_pkey + (int64_t)((kt % kKeysPerPage) + n) * a.pkey_row_bytes + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = *(const bf16x8*)(kp + ks * 32);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
+    }
+  };
+  bf16x8 cur[KS], nxt[KS];
+  if (kb < kend) load(kb, cur);
+  for (int64_t kt = kb; kt < kend; kt += 32) {
+    if (kt + 32 < kend) load(kt + 32, nxt);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], cur[ks], acc, 0, 0, 0);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < H; ++i) s = __builtin_fmaf(wv[i], __builtin_fmaxf(acc[i], 0.f), s);
+    const int64_t key = kt + n;
+    if (g == 0 && key < ke) out[key] = key < nc ? (page_at(kt) >= 0 ? s : __builtin_nanf("")) : ninf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+  }
+  // keys past the compressed length
+  for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) out[key] = ninf;
+}
+
+// Per-row kernel: wave w of workgroup (key group kg, row group rg) takes row 4 rg + w.
+// The row groups of one key group run on one XCD (workgroups 8 apart).
+template <int H, int D>
+__global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n_rg = (a.n_rows + 3) / 4;
+  const int id = blockIdx.x;
+  const int rg = (id >> 3) % n_rg;
+  const int kg = (id / (8 * n_rg)) * 8 + (id & 7);
+  if (kg >= a.n_kgroups) return;
+  const int row = rg * 4 + wave;
+  if (row >= a.n_rows) return;
+  const int64_t kb = (int64_t)kg * a.keys_per_wg;
+  const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  if (kg == 0 && a.n_valid && lane == 0) a.n_valid[row] = nc_of(a, row);
+  index_one_row<H, D>(a, row, kb, ke, lane);
+}
+
+// ---- tile path -----------------------------------------------------------------------------
+template <int D>
+struct KeyTile {
+  __bf16 k[2][32 * D];   // two 32-key subtiles, 16-byte chunks swizzled by key
+};
+
+// Swizzled position of chunk c of key j in a subtile (chunks of 16 bytes, CH per key).
+template <int CH>
+__device__ __forceinline__ int swz(int j, int c) {
+  return j * CH + (c ^ (j & (CH - 1)));
+}
+
 template <int H, int D, int MT>
-__global__ __launch_bounds__(256, 2) void indexer_kernel(IdxArgs a) {
+__global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   constexpr int RPT = 32 / H;   // query rows per MFMA tile
   constexpr int RH = 16 / H;    // rows per half-wave in the accumulators
   constexpr int KS = D / 16;    // MFMA k-steps
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;      // half-wave
-  const int n = lane & 31;      // key column of this lane / A row of this lane
-  const int wave_row0 = (blockIdx.y * 4 + wave) * (MT * RPT);
+  constexpr int CH = D / 8;     // 16-byte chunks per key
+  constexpr int ROWS = 4 * MT * RPT;
+  constexpr int kMaxPages = 40;
+  __shared__ KeyTile<D> kt_lds;
+  __shared__ int32_t pg_lds[kMaxPages];
+  __shared__ int32_t uniform_flag;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int row_base = blockIdx.y * ROWS;
+  const int64_t kb = (int64_t)blockIdx.x * a.keys_per_wg;
+  const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  const int wave_row0 = row_base + wave * (MT * RPT);
+
+  if (blockIdx.x == 0 && a.n_valid && tid < ROWS && row_base + tid < a.n_rows)
+    a.n_valid[row_base + tid] = nc_of(a, row_base + tid);
+
+  // all rows of the workgroup valid and of one stream?
+  if (tid == 0) uniform_flag = 1;
+  __syncthreads();
+  const int b0 = a.row_stream[row_base < a.n_rows ? row_base : a.n_rows - 1];
+  if (tid < ROWS && (row_base + tid >= a.n_rows || a.row_stream[row_base + tid] != b0)) uniform_flag = 0;
+  __syncthreads();
+  if (!uniform_flag) {
+    // per-row path: each wave takes rows of the workgroup in turn
+    for (int rr = wave; rr < ROWS; rr += 4) {
+      const int row = row_base + rr;
+      if (row < a.n_rows) {
+        if (H == 16) index_one_row<16, D>(a, row, kb, ke, lane);
+        else if (H == 8) index_one_row<8, D>(a, row, kb, ke, lane);
+        else index_one_row<4, D>(a, row, kb, ke, lane);
+      }
+    }
+    return;
+  }
+
+  // largest compressed length of the workgroup's rows: keys past it are -inf only
+  int nc_max = 0;
+  int rnc[MT][RH];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < RH; ++r) rnc[t][r] = nc_of(a, wave_row0 + t * RPT + g * RH + r);
+  for (int rr = 0; rr < ROWS; ++rr) {
+    const int c = nc_of(a, row_base + rr);
+    nc_max = c > nc_max ? c : nc_max;
+  }
+  const int64_t kend = ke < nc_max ? ke : nc_max;
+
+  // page ids of the key range
+  const int p0 = (int)(kb / kKeysPerPage);
+  if (tid < kMaxPages) pg_lds[tid] = page_of(a.v, b0, p0 + tid);
 
   // A fragments: lane supplies A-row m = n; m = 8a + 4b + c maps to tile row
   // b*RH + (4a+c)/H and head (4a+c)%H.
@@ -56,143 +209,114 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IdxArgs a) {
     for (int t = 0; t < MT; ++t) {
       const int row = wave_row0 + t * RPT + trow;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (row < a.n_rows) {
-          afrag[t][ks] = *(const bf16x8*)(a.q + ((int64_t)row * H + head) * D + ks * 16 + g * 8);
-        } else {
-          afrag[t][ks] = bf16x8{};
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        afrag[t][ks] = *(const bf16x8*)(a.q + ((int64_t)row * H + head) * D + ks * 16 + g * 8);
     }
   }
-  // Weights of this lane's accumulators: value i is tile row g*RH + i/H, head i%H.
   float wv[MT][16];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = wave_row0 + t * RPT + g * RH + i / H;
-      wv[t][i] = row < a.n_rows ? a.w[(int64_t)row * H + (i % H)] : 0.f;
-    }
-  }
-  // Wave-uniform row facts.
-  int rstream[MT][RPT], rnc[MT][RPT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int row = wave_row0 + t * RPT + j;
-      int nc = -1, st = 0;
-      if (row < a.n_rows) {
-        const int pos = a.row_pos[row];
-        st = a.row_stream[row];
-        nc = pos >= 0 ? (int)((int64_t)pos / kPoolRatio + 1 < a.ld ? pos / kPoolRatio + 1 : a.ld) : 0;
-      }
-      rstream[t][j] = __builtin_amdgcn_readfirstlane(st);
-      rnc[t][j] = __builtin_amdgcn_readfirstlane(nc);
-    }
-  }
-  if (blockIdx.x == 0 && a.n_valid && lane < MT * RPT) {
-    const int row = wave_row0 + lane;
-    if (row < a.n_rows) {
-      const int pos = a.row_pos[row];
-      a.n_valid[row] = pos >= 0 ? (int)((int64_t)pos / kPoolRatio + 1 < a.ld ? pos / kPoolRatio + 1 : a.ld) : 0;
-    }
-  }
+    for (int i = 0; i < 16; ++i) wv[t][i] = a.w[(int64_t)(wave_row0 + t * RPT + g * RH + i / H) * H + (i % H)];
+  __syncthreads();
 
-  const int64_t kb = (int64_t)blockIdx.x * a.keys_per_wg;
-  const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  // global -> LDS loads of one subtile: CH*32 chunks, 64 per wave-wide load; the lane
+  // that fills swizzled position p loads the chunk that belongs there.
+  auto issue = [&](int64_t kt, int buf) {
+    const int pg = pg_lds[(int)(kt / kKeysPerPage) - p0];
+    for (int i = wave; i < CH * 32 / 64; i += 4) {
+      const int p = i * 64 + lane;           // swizzled position
+      const int j = p / CH, c = (p % CH) ^ (j & (CH - 1));
+      const char* src = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey +
+                                      (int64_t)((kt % kKeysPerPage) + j) * a.pkey_row_bytes + c * 16
+                                : a.v.pool + c * 16;   // any readable bytes: rows of a missing page become NaN
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&kt_lds.k[buf][i * 64 * 8], 16, 0, 0);
+    }
+  };
+
   const float ninf = -__builtin_inff();
   const float qnan = __builtin_nanf("");
-
-  for (int64_t kt = kb; kt < ke; kt += 32) {
-    const int pidx = (int)(kt / kKeysPerPage);
-    const int slot0 = (int)(kt % kKeysPerPage);
+  // a subtile's scores are stored one iteration late, so the barrier that waits for
+  // the next subtile's keys does not also wait for fresh stores
+  float pend[MT][RH];
+  int64_t pend_kt = -1;
+  auto flush = [&]() {
+    if (pend_kt < 0) return;
+    const int64_t key = pend_kt + n;
+    if (key >= ke) return;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < RH; ++r) a.logits[(int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ld + key] = pend[t][r];
+  };
+  int buf = 0;
+  if (kb < kend) issue(kb, 0);
+  for (int64_t kt = kb; kt < kend; kt += 32) {
+    __syncthreads();   // this subtile has landed; the other buffer is free
+    if (kt + 32 < kend) issue(kt + 32, buf ^ 1);
+    flush();
+    bf16x8 bfrag[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bfrag[ks] = *(const bf16x8*)&kt_lds.k[buf][swz<CH>(n, 2 * ks + g) * 8];
+    const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
     const int64_t key = kt + n;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      int pg[RPT];
-      bool need[RPT];
+      f32x16 acc = {};
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        need[j] = rnc[t][j] > kt;
-        pg[j] = need[j] ? page_of(a.v, rstream[t][j], pidx) : -2;
-      }
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[t][ks], bfrag[ks], acc, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        // rows past their compressed length for the whole tile: -inf only
-        const int row = wave_row0 + t * RPT + j;
-        if (rnc[t][j] >= 0 && !need[j] && (j / RH) == g && key < a.ld)
-          a.logits[(int64_t)row * a.ld + key] = ninf;
-      }
+      for (int r = 0; r < RH; ++r) {
+        float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        if (!need[j]) continue;
-        bool leader = true;
-#pragma unroll
-        for (int jj = 0; jj < j; ++jj)
-          if (need[jj] && pg[jj] == pg[j]) leader = false;
-        if (!leader) continue;
-        f32x16 acc = {};
-        if (pg[j] >= 0) {
-          const char* kp = cache_block(a.v, pg[j]) + a.off_pkey +
-                           (int64_t)(slot0 + n) * a.pkey_row_bytes + g * 16;
-          bf16x8 bfrag[KS];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) bfrag[ks] = *(const bf16x8*)(kp + ks * 32);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[t][ks], bfrag[ks], acc, 0, 0, 0);
-        }
-        // epilogue: this lane holds rows g*RH + r (r < RH), all heads, key `key`
-#pragma unroll
-        for (int r = 0; r < RH; ++r) {
-          const int tr = g * RH + r;
-          // wave-uniform membership test per tile row, selected per half
-          bool mine = false;
-          int ncr = 0;
-#pragma unroll
-          for (int jj = 0; jj < RPT; ++jj) {
-            if (jj == tr) {
-              mine = need[jj] && pg[jj] == pg[j];
-              ncr = rnc[t][jj];
-            }
-          }
-          if (!mine || key >= a.ld) continue;
-          float s = 0.f;
-#pragma unroll
-          for (int h = 0; h < H; ++h) s = __builtin_fmaf(wv[t][r * H + h], __builtin_fmaxf(acc[r * H + h], 0.f), s);
-          const int row = wave_row0 + t * RPT + tr;
-          a.logits[(int64_t)row * a.ld + key] = key < ncr ? (pg[j] >= 0 ? s : qnan) : ninf;
-        }
+        for (int h = 0; h < H; ++h) s = __builtin_fmaf(wv[t][r * H + h], __builtin_fmaxf(acc[r * H + h], 0.f), s);
+        pend[t][r] = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
       }
     }
+    pend_kt = kt;
+    buf ^= 1;
   }
-}
-
-template <int H, int D, int MT>
-static void launch_one(const IdxArgs& a, int rows_per_wg, hipStream_t st) {
-  const int64_t kgroups = (a.ld + a.keys_per_wg - 1) / a.keys_per_wg;
-  const int rgroups = (a.n_rows + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((indexer_kernel<H, D, MT>), dim3((unsigned)kgroups, (unsigned)rgroups), dim3(256), 0, st, a);
+  flush();
+  // keys past every row's compressed length
+  const int64_t kf = kend > kb ? kend : kb;
+  for (int rr = wave; rr < ROWS; rr += 4)
+    for (int64_t key = kf + lane; key < ke; key += 64) a.logits[(int64_t)(row_base + rr) * a.ld + key] = ninf;
 }
 
 template <int H, int D>
-static void launch_hd(const IdxArgs& a0, int32_t n_rows, hipStream_t st) {
-  IdxArgs a = a0;
+static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
   constexpr int RPT = 32 / H;
-  // Two tiles per wave when there are rows to fill them; one for small batches.
-  const int mt = n_rows >= 8 * 4 * RPT ? 2 : 1;
-  const int rows_per_wg = 4 * mt * RPT;
-  const int64_t rgroups = (n_rows + rows_per_wg - 1) / rows_per_wg;
-  // about 2048 workgroups in all, each over a multiple of 32 keys
-  int64_t kpw = (a.ld * rgroups + 2047) / 2048;
-  kpw = (kpw + 31) / 32 * 32;
-  if (kpw < 32) kpw = 32;
-  if (kpw > 4096) kpw = 4096;
-  a.keys_per_wg = (int32_t)kpw;
-  if (mt == 2) launch_one<H, D, 2>(a, rows_per_wg, st);
-  else launch_one<H, D, 1>(a, rows_per_wg, st);
+  if (n_rows >= 64) {
+    constexpr int MT = 2;
+    constexpr int ROWS = 4 * MT * RPT;
+    const int64_t rgroups = (n_rows + ROWS - 1) / ROWS;
+    // about 2,048 workgroups, each over a multiple of 128 keys (at most 4,096)
+    int64_t kpw = (a.ld * rgroups + 2047) / 2048;
+    kpw = (kpw + 127) / 128 * 128;
+    if (kpw < 128) kpw = 128;
+    if (kpw > 4096) kpw = 4096;
+    a.keys_per_wg = (int32_t)kpw;
+    const int64_t kgroups = (a.ld + kpw - 1) / kpw;
+    a.n_kgroups = (int32_t)kgroups;
+    if (rgroups > 65535) return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows for one launch");
+    hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT>), dim3((unsigned)kgroups, (unsigned)rgroups), dim3(256), 0,
+                       st, a);
+  } else {
+    // each wave one row; about 1,024 waves in all; a wave's range spans at most 64 pages
+    const int n_rg = (n_rows + 3) / 4;
+    int64_t kpw = (a.ld * n_rows + 1023) / 1024;
+    kpw = (kpw + 127) / 128 * 128;
+    if (kpw < 128) kpw = 128;
+    if (kpw > 64 * 128) kpw = 64 * 128;
+    a.keys_per_wg = (int32_t)kpw;
+    const int64_t kgroups = (a.ld + kpw - 1) / kpw;
+    a.n_kgroups = (int32_t)kgroups;
+    const int64_t grid = ((kgroups + 7) / 8) * 8 * n_rg;
+    if (grid > 0x7fffffffLL) return set_error(TF_E_RANGE, "tf_indexer_logits: too many keys for one launch");
+    hipLaunchKernelGGL((indexer_rows_kernel<H, D>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  }
+  return TF_OK;
 }
 
 tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
@@ -210,19 +334,20 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, con
   a.logits = logits;
   a.ld = ld;
   a.n_valid = n_valid;
-  a.keys_per_wg = 32;
+  a.keys_per_wg = 128;
+  a.n_kgroups = 1;
   const int D = p->g.index_dim;
-  if ((ld + 2047) / 2048 * ((n_rows + 7) / 8) > 0x7fffffffLL)
-    return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows x keys for one launch");
+  tf_status s;
   if (D == 128) {
-    if (n_heads == 16) launch_hd<16, 128>(a, n_rows, st);
-    else if (n_heads == 8) launch_hd<8, 128>(a, n_rows, st);
-    else launch_hd<4, 128>(a, n_rows, st);
+    if (n_heads == 16) s = launch_hd<16, 128>(a, n_rows, st);
+    else if (n_heads == 8) s = launch_hd<8, 128>(a, n_rows, st);
+    else s = launch_hd<4, 128>(a, n_rows, st);
   } else {
-    if (n_heads == 16) launch_hd<16, 64>(a, n_rows, st);
-    else if (n_heads == 8) launch_hd<8, 64>(a, n_rows, st);
-    else launch_hd<4, 64>(a, n_rows, st);
+    if (n_heads == 16) s = launch_hd<16, 64>(a, n_rows, st);
+    else if (n_heads == 8) s = launch_hd<8, 64>(a, n_rows, st);
+    else s = launch_hd<4, 64>(a, n_rows, st);
   }
+  if (s != TF_OK) return s;
   return launch_status("tf_indexer_logits");
 }
 

@@ -112,10 +112,12 @@ def run_step(wl, plan, view, rows, ld, scale, k=None):
     return host(logits), host(nv), host(blocks), host(out), host(lse)
 
 
+@pytest.mark.parametrize("hq", [8, 32])
 @pytest.mark.parametrize("scale", SCALES)
-def test_full_step_against_oracle(tiny_pool, scale):
-    _log(f"step: indexer -> top-k -> attention, tiny, scale {scale:.4f}")
+def test_full_step_against_oracle(tiny_pool, scale, hq):
+    _log(f"step: indexer -> top-k -> attention, tiny, {hq} heads, scale {scale:.4f}")
     wl, plan, P = tiny_pool
+    wl = _with_heads(wl, hq)
     rows = wl.rows
     ld = 512
     lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, ld, scale)
@@ -127,6 +129,24 @@ def test_full_step_against_oracle(tiny_pool, scale):
     check_topk_against_oracle(blk, ref_l, nv, wl.k)
     ro, rl = ow.attention(wl, 0, rows, blk, scale)
     check_attention(out, lse, ro, rl, "tiny")
+
+
+def _with_heads(wl, hq):
+    import copy
+    w2 = copy.copy(wl)
+    w2.Hq = hq
+    return w2
+
+
+@pytest.mark.parametrize("hq", [8, 32])
+def test_decode_rows_split_paths(tiny_pool, hq):
+    _log(f"decode rows only (split block lists, merge kernel), tiny, {hq} heads")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, hq)
+    rows = [(0, 2047), (1, 2047), (1, 1000), (0, 3)]
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, 512, 24.0)
+    ro, rl = ow.attention(wl, 0, rows, blk, 24.0)
+    check_attention(out, lse, ro, rl, "decode split")
 
 
 def test_paged_equals_contiguous_bitwise(tiny_pool):
