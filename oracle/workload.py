@@ -34,15 +34,22 @@ def keys_of(wl, c: int, b: int, n: int) -> np.ndarray:
     return bf16_to_f64(wl.pkey_bits(c, b, np.arange(n)))
 
 
-def logits(wl, c: int, rows, ld: int) -> np.ndarray:
-    q = bf16_to_f64(wl.iq_bits(c, rows))
-    w = wl.weights(c, rows).astype(np.float64)
+def row_keys(wl, c: int, rows, ld: int):
+    """Each row's pooled keys (one array per distinct stream, shared between its rows)."""
     keys, cache = [], {}
     for (b, t) in rows:
         n = min(n_compressed(t), ld)
         if cache.get(b, (None, 0))[1] < n:
             cache[b] = (keys_of(wl, c, b, n), n)
         keys.append(cache[b][0])
+    return keys
+
+
+def logits(wl, c: int, rows, ld: int, keys=None) -> np.ndarray:
+    q = bf16_to_f64(wl.iq_bits(c, rows))
+    w = wl.weights(c, rows).astype(np.float64)
+    if keys is None:
+        keys = row_keys(wl, c, rows, ld)
     return indexer_logits(q, w, keys, [t for _, t in rows], ld)
 
 

@@ -26,15 +26,17 @@ def bf16_host(t: torch.Tensor) -> np.ndarray:
     return bf16_to_f64(host(t.view(torch.int16)).view(np.uint16))
 
 
-def logits_bound(wl, c, rows, ld):
+def logits_bound(wl, c, rows, ld, keys=None):
     """A[r, j] of the logit tolerance (fp64)."""
     from oracle import workload as ow
     q = np.abs(bf16_to_f64(wl.iq_bits(c, rows)))
     w = np.abs(wl.weights(c, rows).astype(np.float64))
+    if keys is None:
+        keys = ow.row_keys(wl, c, rows, ld)
     out = np.zeros((len(rows), ld))
     for r, (b, t) in enumerate(rows):
         n = min(t // 4 + 1, ld)
-        k = np.abs(ow.keys_of(wl, c, b, n))
+        k = np.abs(keys[r][:n])
         out[r, :n] = w[r] @ (q[r] @ k.T)
     return out
 

@@ -1,0 +1,195 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench
+times: every row where the oracle computes it in seconds, sampled rows otherwise,
+and properties that hold at any size (top-k exact on the GPU's own logits; resumed
+== fresh bit for bit; unwritten rows never read)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_page_table_amd as tf
+from oracle import topk_blocks as oracle_topk
+from oracle import workload as ow
+from oracle.attention import sparse_mla_row
+from oracle.indexer import indexer_logits
+from synth import bf16_to_f64
+from synth.configs import adaptive_prefill, decode_batch, prefill_chunk, shared_prefix_decode
+from synth.device import NAN16, alloc_pool, populate, query_inputs, write_rows
+from tests.gpu_common import (check_attention, check_logits, check_topk_against_oracle, host, logits_bound,
+                              topk_on_values)
+
+pytestmark = pytest.mark.gpu
+SCALES = [1.0 / math.sqrt(576.0), 24.0]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def gpu_step(plan, view, wl, c, rows, ld, scales, q_rows=None, stream_override=None):
+    """indexer -> top-k -> attention for the given rows; returns host copies."""
+    rs, rp, iq, w, q = query_inputs(wl, c, q_rows or rows)
+    if stream_override is not None:
+        rs = torch.full_like(rs, stream_override)
+    R = len(rows)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, view, rs, rp, iq, w, logits, n_valid=nv)
+    blocks = torch.empty((R, wl.k), dtype=torch.int32, device="cuda")
+    tf.topk_blocks(logits, nv, wl.k, blocks)
+    outs = []
+    for sc in scales:
+        out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+        tf.sparse_mla_attn(plan, view, rs, rp, q, sc, blocks, out, lse)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    return logits, host(nv), host(blocks), outs
+
+
+def test_decode_batch_full():
+    """8 streams x 131,072 tokens, shuffled pages: every row against the oracle."""
+    wl = decode_batch(0)
+    _log(f"decode batch: populating {wl.n_pages} pages")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows, ld = wl.rows, 32768
+    lg_t, nv, blk, outs = gpu_step(plan, P.view(), wl, 0, rows, ld, SCALES)
+    lg = host(lg_t)
+    _log("decode batch: oracle logits")
+    ref = ow.logits(wl, 0, rows, ld)
+    check_logits(lg, ref, logits_bound(wl, 0, rows, ld), "decode batch")
+    assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+    check_topk_against_oracle(blk, ref, nv, wl.k)
+    for sc, (out, lse) in zip(SCALES, outs):
+        _log(f"decode batch: oracle attention, scale {sc:.4f}")
+        ro, rl = ow.attention(wl, 0, rows, blk, sc)
+        check_attention(host(out), host(lse), ro, rl, f"decode batch scale {sc}")
+
+
+def test_prefill_chunk_full():
+    """T = 2,048 rows against L = 100,000: logits and attention on sampled rows, top-k
+    exact on every row's GPU logits."""
+    wl = prefill_chunk(0)
+    _log("prefill chunk: populating")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows, ld = wl.rows, 25000
+    lg_t, nv, blk, outs = gpu_step(plan, P.view(), wl, 0, rows, ld, SCALES)
+    lg = host(lg_t)
+    _log("prefill chunk: exact top-k of every row's logits")
+    assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+    rng = np.random.default_rng(7)
+    sample = sorted(set([0, 1, 511, 1024, 2046, 2047] + rng.choice(2048, 10, replace=False).tolist()))
+    srows = [rows[i] for i in sample]
+    _log(f"prefill chunk: oracle on {len(sample)} sampled rows")
+    ref = ow.logits(wl, 0, srows, ld)
+    check_logits(lg[sample], ref, logits_bound(wl, 0, srows, ld), "prefill sampled")
+    check_topk_against_oracle(blk[sample], ref, nv[sample], wl.k)
+    for sc, (out, lse) in zip(SCALES, outs):
+        ro, rl = ow.attention(wl, 0, srows, blk[sample], sc)
+        check_attention(host(out)[sample], host(lse)[sample], ro, rl, f"prefill scale {sc}")
+
+
+def test_shared_prefix_decode_12_caches():
+    """8 streams sharing 2,048 pages (1,048,576 tokens) plus a private tail page each, 12
+    caches: every cache runs; caches 0, 5 and 11 are checked row by row."""
+    wl = shared_prefix_decode(0)
+    plan = tf.kv_pool_plan(tf.geom(wl.n_caches, wl.Dk))
+    _log(f"shared prefix: pool {wl.n_pages} pages x {plan.page_bytes} B")
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows = wl.rows
+    ld = max(t // 4 + 1 for _, t in rows)
+    for c in range(wl.n_caches):
+        lg_t, nv, blk, outs = gpu_step(plan, P.view(c), wl, c, rows, ld, [24.0])
+        lg = host(lg_t)
+        assert np.array_equal(blk, topk_on_values(lg, nv, wl.k)), f"cache {c}"
+        if c not in (0, 5, 11):
+            continue
+        _log(f"shared prefix: oracle, cache {c}")
+        shared = ow.keys_of(wl, c, 0, wl.shared_tokens // 4)      # one copy of the shared keys
+        keys = []
+        for b, t in rows:
+            n = t // 4 + 1
+            tail = bf16_to_f64(wl.pkey_bits(c, b, np.arange(wl.shared_tokens // 4, n)))
+            keys.append(np.concatenate([shared, tail]))
+        ref = ow.logits(wl, c, rows, ld, keys=keys)
+        check_logits(lg, ref, logits_bound(wl, c, rows, ld, keys=keys), f"cache {c}")
+        check_topk_against_oracle(blk, ref, nv, wl.k)
+        ro, rl = ow.attention(wl, c, rows, blk, 24.0)
+        out, lse = outs[0]
+        check_attention(host(out), host(lse), ro, rl, f"cache {c}")
+
+
+def test_adaptive_prefill_fp8_snapshot_resume():
+    """390,000-token prompt in fp8 rows, chunk(L) = clamp(round_down_256(2e8 / L), 256, 2048);
+    sampled rows of several chunks against the oracle; then the first 262,144 rows are
+    snapshot into fresh pages, one 2,048-token chunk is resumed there, and it equals
+    the same rows of the fresh run bit for bit."""
+    wl = adaptive_prefill(0)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    P = alloc_pool(wl, plan)
+    N = wl.lengths[0]
+    view = P.view()
+    L = 0
+    n_chunks = 0
+    checks = []
+    rng = np.random.default_rng(11)
+    _log("adaptive prefill: running the chunk schedule")
+    while L < N:
+        T = tf.prefill_chunk(L, N - L)
+        write_rows(P, 0, 0, L, L + T)
+        rows = [(0, t) for t in range(L, L + T)]
+        ld = (L + T - 1) // 4 + 1
+        lg_t, nv, blk, outs = gpu_step(plan, view, wl, 0, rows, ld, [24.0])
+        if n_chunks in (0, 1, 47, 48, 100, 200, 463) or L + T == N:
+            sel = sorted(set([0, T - 1] + rng.choice(T, 2, replace=False).tolist()))
+            checks.append((L, T, ld, [rows[i] for i in sel], host(lg_t)[sel], nv[sel], blk[sel],
+                           host(outs[0][0])[sel], host(outs[0][1])[sel]))
+        assert not torch.isnan(outs[0][0]).any(), f"NaN in chunk at {L}"
+        L += T
+        n_chunks += 1
+    assert n_chunks == 464
+    all_keys = ow.keys_of(wl, 0, 0, (N - 1) // 4 + 1)      # stream 0's keys, generated once
+    for (L0, T, ld, srows, lg, nv, blk, out, lse) in checks:
+        _log(f"adaptive prefill: oracle on chunk [{L0}, {L0 + T})")
+        keys = [all_keys] * len(srows)
+        ref = ow.logits(wl, 0, srows, ld, keys=keys)
+        check_logits(lg, ref, logits_bound(wl, 0, srows, ld, keys=keys), f"chunk {L0}")
+        assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+        check_topk_against_oracle(blk, ref, nv, wl.k)
+        ro, rl = ow.attention(wl, 0, srows, blk, 24.0)
+        check_attention(out, lse, ro, rl, f"chunk {L0}")
+
+    at = 262144
+    _log("adaptive prefill: snapshot of the first 262,144 rows, resume one chunk")
+    src = torch.tensor([0], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([1], dtype=torch.int32, device="cuda")
+    tf.snapshot_copy(plan, view, view, src, dst, at)
+    torch.cuda.synchronize()
+    # snapshot bytes: every copied page block equals its source; stream 1's rows past at are poison
+    pool = host(P.pool)
+    pb = plan.page_bytes
+    pt = wl.pt
+    for i in [0, 1, 255, 511]:
+        a = pool[pt[0, i] * pb:(pt[0, i] + 1) * pb]
+        b = pool[pt[1, i] * pb:(pt[1, i] + 1) * pb]
+        assert np.array_equal(a, b), f"page {i}"
+    tail = pool[pt[1, 512] * pb:(pt[1, 512] + 1) * pb].view(np.uint16)
+    assert np.all(tail == NAN16)
+    # resume: rows [at, at + 2048) of stream 1 from the same generator rows as stream 0
+    write_rows(P, 0, 1, at, at + 2048, owner=0)
+    rows = [(0, t) for t in range(at, at + 2048)]
+    ld = (at + 2047) // 4 + 1
+    fresh = gpu_step(plan, view, wl, 0, rows, ld, [24.0])
+    resumed = gpu_step(plan, view, wl, 0, rows, ld, [24.0], stream_override=1)
+    assert torch.equal(fresh[0], resumed[0])
+    assert np.array_equal(fresh[2], resumed[2])
+    assert torch.equal(fresh[3][0][0], resumed[3][0][0])
+    assert torch.equal(fresh[3][0][1], resumed[3][0][1])
+    # no poisoned byte reached the outputs
+    assert not torch.isnan(resumed[3][0][0]).any()
