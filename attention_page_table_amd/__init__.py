@@ -94,6 +94,31 @@ def _check(status: int):
         raise TFError(status, lib().tf_last_error().decode())
 
 
+class Launch:
+    """A device call whose arguments were marshalled once (pointers, sizes, stream);
+    calling it enqueues the same work again, on the stream given when it was made.
+    The tensors passed in must outlive it; ``keep`` holds the ones the call itself
+    allocated (workspaces)."""
+    __slots__ = ("_f", "_a", "keep")
+
+    def __init__(self, name: str, args: tuple, keep=()):
+        self._f = getattr(lib(), name)
+        self._a = args
+        self.keep = keep
+
+    def __call__(self):
+        s = self._f(*self._a)
+        if s != TF_OK:
+            raise TFError(s, lib().tf_last_error().decode())
+
+
+def _run(name: str, args: tuple, prepare: bool, keep=()):
+    if prepare:
+        return Launch(name, args, keep)
+    _check(getattr(lib(), name)(*args))
+    return None
+
+
 # ------------------------------------------------------------------ host calls
 def geom(n_caches=1, index_dim=128, fp8=False, rope_dim=64, page_rows=512, latent_dim=512, pool_ratio=4):
     return tf_geom(n_caches, page_rows, latent_dim, rope_dim, pool_ratio, index_dim,
@@ -140,32 +165,33 @@ def view(pool, pt, pt_stride: int, n_pages: int, cache: int = 0, n_streams: int 
 
 
 def latent_write(plan, dst, row_stream, row_pos, latent, rope, row_scale=None,
-                 pkey_stream=None, pkey_idx=None, pkeys=None, stream=None):
+                 pkey_stream=None, pkey_idx=None, pkeys=None, stream=None, prepare=False):
     n_rows = 0 if row_stream is None else row_stream.numel()
     n_pk = 0 if pkey_stream is None else pkey_stream.numel()
-    _check(lib().tf_latent_write(ctypes.byref(plan), dst, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(latent),
-                                 _ptr(row_scale), _ptr(rope), n_pk, _ptr(pkey_stream), _ptr(pkey_idx),
-                                 _ptr(pkeys), _stream(stream)))
+    return _run("tf_latent_write", (ctypes.byref(plan), dst, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(latent),
+                                    _ptr(row_scale), _ptr(rope), n_pk, _ptr(pkey_stream), _ptr(pkey_idx),
+                                    _ptr(pkeys), _stream(stream)), prepare)
 
 
-def indexer_logits(plan, keys, row_stream, row_pos, q, w, logits, n_valid=None, stream=None):
+def indexer_logits(plan, keys, row_stream, row_pos, q, w, logits, n_valid=None, stream=None, prepare=False):
     n_rows, H = w.shape
-    _check(lib().tf_indexer_logits(ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
-                                   _ptr(w), H, _ptr(logits), logits.shape[1], _ptr(n_valid), _stream(stream)))
+    return _run("tf_indexer_logits", (ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                      _ptr(w), H, _ptr(logits), logits.shape[1], _ptr(n_valid), _stream(stream)),
+                prepare)
 
 
 def topk_workspace_bytes(n_rows: int, ld: int, k: int) -> int:
     return int(lib().tf_topk_workspace_bytes(n_rows, ld, k))
 
 
-def topk_blocks(logits, n_valid, k: int, blocks, ws=None, stream=None):
+def topk_blocks(logits, n_valid, k: int, blocks, ws=None, stream=None, prepare=False):
     n_rows, ld = logits.shape
     need = topk_workspace_bytes(n_rows, ld, k)
     if need and ws is None:
         import torch
         ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
-    _check(lib().tf_topk_blocks(_ptr(logits), ld, n_rows, _ptr(n_valid), k, _ptr(blocks), _ptr(ws),
-                                0 if ws is None else ws.numel(), _stream(stream)))
+    return _run("tf_topk_blocks", (_ptr(logits), ld, n_rows, _ptr(n_valid), k, _ptr(blocks), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)), prepare, keep=(ws,))
 
 
 def attn_workspace_bytes(n_rows: int, n_heads: int, k: int) -> int:
@@ -173,18 +199,19 @@ def attn_workspace_bytes(n_rows: int, n_heads: int, k: int) -> int:
 
 
 def sparse_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, blocks, out, lse=None, ws=None,
-                    stream=None):
+                    stream=None, prepare=False):
     n_rows, n_heads = q.shape[0], q.shape[1]
     k = blocks.shape[1]
     need = attn_workspace_bytes(n_rows, n_heads, k)
     if need and ws is None:
         import torch
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib().tf_sparse_mla_attn(ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
-                                    n_heads, float(softmax_scale), _ptr(blocks), k, _ptr(out), _ptr(lse), _ptr(ws),
-                                    0 if ws is None else ws.numel(), _stream(stream)))
+    return _run("tf_sparse_mla_attn", (ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                       n_heads, float(softmax_scale), _ptr(blocks), k, _ptr(out), _ptr(lse),
+                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+                prepare, keep=(ws,))
 
 
-def snapshot_copy(plan, src, dst, src_stream, dst_stream, at: int, stream=None):
-    _check(lib().tf_snapshot_copy(ctypes.byref(plan), src, dst, src_stream.numel(), _ptr(src_stream),
-                                  _ptr(dst_stream), at, _stream(stream)))
+def snapshot_copy(plan, src, dst, src_stream, dst_stream, at: int, stream=None, prepare=False):
+    return _run("tf_snapshot_copy", (ctypes.byref(plan), src, dst, src_stream.numel(), _ptr(src_stream),
+                                     _ptr(dst_stream), at, _stream(stream)), prepare)

@@ -259,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       bfrag[ks] = *(const bf16x8*)&kt_lds.k[buf][swz<CH>(n, 2 * ks + g) * 8];
+    __builtin_amdgcn_sched_barrier(0);
     const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
     const int64_t key = kt + n;
 #pragma unroll

@@ -5,19 +5,22 @@
 // topk(union) == topk(union of per-block topk).
 //
 // Design: a workgroup of 1,024 threads owns a segment of up to 32,768 keys held in
-// registers (each thread a contiguous run of E keys, loaded with 16-byte loads).
-// Logits become order-preserving 32-bit keys. A most-significant-digit radix
-// select in three passes (11 + 11 + 10 bits, 2,048-bin LDS histograms) finds the
-// k-th largest key T and how many keys equal to T belong to the top k; an ordered
-// compaction (two block scans over the threads' runs) then writes the selected
-// indices ascending, taking keys equal to T lowest index first. No sort is needed
-// because the output order is by index. Long rows: stage 1 selects per key block,
-// stage 2 merges the blocks' candidates (kept in index order).
+// registers; wave w owns the contiguous index range [w*64E, (w+1)*64E) and its lane l
+// holds indices w*64E + 64e + l (coalesced loads). Logits become order-preserving
+// 32-bit keys. The bits above the highest bit in which the segment's keys differ
+// (from OR/AND reductions) are common; a most-significant-digit radix select over
+// the rest, in passes of at most 11 bits with 2,048-bin LDS histograms, finds the
+// k-th largest key T and how many keys equal to T belong to the top k. An ordered
+// compaction with wave ballots then writes the selected indices ascending, taking
+// keys equal to T lowest index first. No sort is needed because the output order is
+// by index. Long rows: stage 1 selects per key block, stage 2 merges the blocks'
+// candidates (kept in index order).
 #include "common.h"
 
 namespace tf {
 
 constexpr int kNT = 1024;  // threads per workgroup
+constexpr int kWaves = kNT / 64;
 constexpr int kBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -26,26 +29,42 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, row_mask, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: row shifts, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u<0x111>(x);        // row_shr:1
+  x += dpp_u<0x112>(x);        // row_shr:2
+  x += dpp_u<0x114>(x);        // row_shr:4
+  x += dpp_u<0x118>(x);        // row_shr:8
+  x += dpp_u<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_u<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 struct SelShared {
   uint32_t hist[kBins];
-  uint32_t wsum[kNT / 64];
-  uint32_t bin, rem;
+  uint32_t wsum[kWaves];
+  uint32_t wgt[kWaves], weq[kWaves];
+  uint32_t bin, rem, orv, andv;
 };
 
-// Exclusive scan over the workgroup; `total` receives the sum.
+// Exclusive prefix over the workgroup's threads; `total` receives the sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wid] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kNT / 64; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     const uint32_t s = wsum[w];
     base += w < wid ? s : 0u;
     tot += s;
@@ -59,18 +78,51 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
 // valid key), rem = how many keys equal to T belong to the top k.
 template <int E>
 __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uint32_t& T, uint32_t& rem) {
-  uint32_t prefix = 0, mask = 0, r = (uint32_t)k;
+  // common leading bits of the valid keys
+  uint32_t o = 0u, an = 0xFFFFFFFFu;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+  for (int e = 0; e < E; ++e)
+    if (key[e] != 0u) {
+      o |= key[e];
+      an &= key[e];
+    }
+  if (threadIdx.x == 0) {
+    sh.orv = 0u;
+    sh.andv = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  // wave reduction, then one LDS atomic per wave
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    o |= __shfl_xor(o, s, 64);
+    an &= __shfl_xor(an, s, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicOr(&sh.orv, o);
+    atomicAnd(&sh.andv, an);
+  }
+  __syncthreads();
+  const uint32_t diff = sh.orv ^ sh.andv;
+  if (diff == 0u) {  // every valid key equal
+    T = sh.orv;
+    rem = (uint32_t)k;
+    return;
+  }
+  const int hb = 31 - __builtin_clz(diff);   // highest differing bit
+  uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = sh.andv & mask, r = (uint32_t)k;
+  int top = hb + 1;   // bits [0, top) remain
+  while (top > 0) {
+    const int width = top > 11 ? 11 : top;
+    const int shift = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
     for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1u);
     __syncthreads();
-    // suffix sums: thread t owns bins 2047 - 2t and 2046 - 2t (descending)
+    // suffix sums over bins: thread t owns bins 2047 - 2t and 2046 - 2t (descending)
     const uint32_t c0 = sh.hist[kBins - 1 - 2 * threadIdx.x], c1 = sh.hist[kBins - 2 - 2 * threadIdx.x];
     uint32_t tot;
     const uint32_t above = block_exclusive_scan(c0 + c1, sh.wsum, tot);
@@ -85,33 +137,45 @@ __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uin
     prefix |= sh.bin << shift;
     mask |= dmask << shift;
     r = sh.rem;
+    top = shift;
     __syncthreads();
   }
   T = prefix;
   rem = r;
 }
 
-// Ordered compaction of a thread's contiguous run: emit(pos, e) for each selected key.
+// Ordered compaction: emit(pos, e) for every selected key, in index order
+// (wave-major, then e, then lane).
 template <int E, typename Emit>
 __device__ void ordered_select(const uint32_t (&key)[E], uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    gt += key[e] > T;
-    eq += key[e] == T;
+    gt += __builtin_popcountll(__ballot(key[e] > T));
+    eq += __builtin_popcountll(__ballot(key[e] == T));
   }
-  uint32_t tot;
-  const uint32_t eq_before = block_exclusive_scan(eq, sh.wsum, tot);
-  const uint32_t take_eq = eq_before >= rem ? 0u : (rem - eq_before < eq ? rem - eq_before : eq);
-  uint32_t pos = block_exclusive_scan(gt + take_eq, sh.wsum, tot);
-  uint32_t took = 0;
+  if (lane == 0) {
+    sh.wgt[wid] = gt;
+    sh.weq[wid] = eq;
+  }
+  __syncthreads();
+  uint32_t eq_base = 0, pos_base = 0;
+  for (int w = 0; w < wid; ++w) {
+    const uint32_t we = sh.weq[w];
+    const uint32_t take = eq_base >= rem ? 0u : (rem - eq_base < we ? rem - eq_base : we);
+    pos_base += sh.wgt[w] + take;
+    eq_base += we;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool eqT = key[e] == T;
-    if (key[e] > T || (eqT && took < take_eq)) {
-      took += eqT;
-      emit(pos++, e);
-    }
+    const bool is_eq = key[e] == T;
+    const uint64_t em = __ballot(is_eq);
+    const bool take = key[e] > T || (is_eq && eq_base + lanes_below(em) < rem);
+    const uint64_t tm = __ballot(take);
+    if (take) emit(pos_base + lanes_below(tm), e);
+    pos_base += __builtin_popcountll(tm);
+    eq_base += __builtin_popcountll(em);
   }
 }
 
@@ -135,22 +199,18 @@ __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
   return nv;
 }
 
-// Keys of [0, n) of a float row, thread t taking the run [t*E, t*E + E).
+// index of this thread's e-th key within the segment
+template <int E>
+__device__ __forceinline__ int seg_index(int e) {
+  return (threadIdx.x >> 6) * 64 * E + e * 64 + (threadIdx.x & 63);
+}
+
 template <int E>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&key)[E]) {
-  const int base = threadIdx.x * E;
-  if ((E % 4) == 0 && ((uintptr_t)row & 15) == 0 && base + E <= n) {
 #pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const float4 v = *(const float4*)(row + base + e);
-      key[e] = order_key(v.x);
-      key[e + 1] = order_key(v.y);
-      key[e + 2] = order_key(v.z);
-      key[e + 3] = order_key(v.w);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(row[base + e]) : 0u;
+  for (int e = 0; e < E; ++e) {
+    const int i = seg_index<E>(e);
+    key[e] = i < n ? order_key(row[i]) : 0u;
   }
 }
 
@@ -169,9 +229,8 @@ __global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
   load_keys<E>(a.logits + (int64_t)r * a.ld, n, key);
   uint32_t T, rem;
   radix_select<E>(key, a.k, sh, T, rem);
-  const int base = threadIdx.x * E;
   ordered_select<E>(key, T, rem, sh, [&](uint32_t pos, int e) {
-    if (pos < (uint32_t)a.k) out[pos] = base + e;
+    if (pos < (uint32_t)a.k) out[pos] = seg_index<E>(e);
   });
 }
 
@@ -201,11 +260,10 @@ __global__ __launch_bounds__(kNT) void topk_stage1_kernel(TopkArgs a) {
   load_keys<E>(row, n, key);
   uint32_t T, rem;
   radix_select<E>(key, a.k, sh, T, rem);
-  const int base = threadIdx.x * E;
   ordered_select<E>(key, T, rem, sh, [&](uint32_t pos, int e) {
     if (pos < (uint32_t)a.k) {
       ck[pos] = key[e];
-      ci[pos] = i0 + base + e;
+      ci[pos] = i0 + seg_index<E>(e);
     }
   });
 }
@@ -228,11 +286,11 @@ __global__ __launch_bounds__(kNT) void topk_stage2_kernel(TopkArgs a) {
   const int32_t* ci = a.ws_idx + (int64_t)r * a.nblk * a.k;
   uint32_t key[E];
   int32_t idx[E];
-  const int base = threadIdx.x * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    key[e] = base + e < n ? ck[base + e] : 0u;
-    idx[e] = base + e < n ? ci[base + e] : -1;
+    const int i = seg_index<E>(e);
+    key[e] = i < n ? ck[i] : 0u;
+    idx[e] = i < n ? ci[i] : -1;
   }
   uint32_t T, rem;
   radix_select<E>(key, a.k, sh, T, rem);
@@ -244,10 +302,10 @@ __global__ __launch_bounds__(kNT) void topk_stage2_kernel(TopkArgs a) {
 // Key-block length for the blocked mode, or 0 for one workgroup per row.
 static int pick_block(int32_t n_rows, int64_t ld, int32_t k) {
   if (ld <= 4096 || (ld <= 32768 && n_rows >= 128)) return 0;
-  // few long rows: blocks of 2,048 .. 32,768 keys so that about 128 workgroups run,
+  // few long rows: blocks of 4,096 .. 32,768 keys so that about 64 workgroups run,
   // with the merged candidates (blocks x k) at most 32,768
-  int64_t B = 2048;
-  while (B < 32768 && n_rows * ((ld + B - 1) / B) > 128) B *= 2;
+  int64_t B = 4096;
+  while (B < 32768 && n_rows * ((ld + B - 1) / B) > 64) B *= 2;
   while (B < 32768 && ((ld + B - 1) / B) * k > 32768) B *= 2;
   if (((ld + B - 1) / B) * k > 32768) return -1;
   return (int)B;

@@ -7,16 +7,27 @@ heads, 16 indexer heads x 128, top-512 blocks:
   tf_latent_write (each stream's new row + its pooled key) -> tf_indexer_logits
   -> tf_topk_blocks -> tf_sparse_mla_attn.
 The page address is computed inside each kernel; the plan is host-side and
-computed once. Inputs are resident in HBM before timing. Consecutive steps
-rotate over independent copies of the pool so that no step finds the previous
-step's rows in the 256 MB Infinity Cache.
+computed once. Inputs are resident in HBM before timing; the launches are
+marshalled once before timing. Consecutive steps rotate over independent copies
+of the pool so that no step finds the previous step's rows in the 256 MB
+Infinity Cache.
 
-Reported: value = selected latent bytes per step / wall time per step (GB/s),
-the dominant kernel against the HBM roofline (durations from HIP events on the
-launch stream), the prefill-chunk indexer (T = 2,048 rows against 25,000 pooled
-keys) against the bf16 MFMA roofline, and the oracle timed on the host cores.
+Reported:
+* value = paged-cache bytes one step reads (every visible pooled key, scanned by
+  the indexer, plus the latent + rope rows of the selected blocks, gathered by
+  the attention) / time per step, in GB/s;
+* the dominant call against the HBM roofline (algorithmic bytes per launch /
+  its average duration from HIP events on the launch stream), with the HBM
+  traffic the rocprofv3 counters measured for it when they match the source;
+* the prefill-chunk indexer (T = 2,048 rows against 25,000 pooled keys) against
+  the bf16 MFMA roofline;
+* the oracle timed on the host cores on a bounded sample of the same step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+
+Profile summaries (no GPU needed; reads rocprofv3's SQLite output):
+    python bench.py --summarize-trace DB --label NAME --command "..."
+    python bench.py --summarize-pmc FETCH_DB WRITE_DB --command "..."
 """
 from __future__ import annotations
 
@@ -25,35 +36,51 @@ import hashlib
 import json
 import math
 import os
+import sqlite3
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+CSRC = os.path.join(ROOT, "attention_page_table_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 512 * 2 + 64 * 2
+CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
+
+# entry point -> (kernels it launches, by name prefix; source file)
+ENTRIES = {
+    "write": (("tf::latent_write_kernel",), "write.hip"),
+    "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
+    "indexer_prefill": (("tf::indexer_tile_kernel",), "indexer.hip"),
+    "topk": (("tf::topk_stage1_kernel", "tf::topk_stage2_kernel", "tf::topk_row_kernel"), "topk.hip"),
+    "attention": (("tf::attn_decode_kernel", "tf::attn_kernel", "tf::attn_merge_kernel"), "attention.hip"),
+}
+TRAFFIC_FILE = "traffic_bench_decode_8x131072_prefill_indexer_2048_at_100000.json"
+CAL_KERNEL = "neg_kernel"      # torch.neg over CAL_BYTES of float32: a plain streaming copy
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(name):
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_name, src_file, launches_note=None):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None when
-    the kernel source changed since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
+def load_traffic(entry):
+    """HBM bytes per launch of an entry point from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    p = os.path.join(PROFILES, TRAFFIC_FILE)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("source_sha256_16") != kernel_hash(src_file):
+    e = d.get("entries", {}).get(entry)
+    if e is None or e.get("source_sha256_16") != source_hash(ENTRIES[entry][1]):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return e.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -64,10 +91,21 @@ def main():
     ap.add_argument("--replicas", type=int, default=6, help="pool copies rotated between steps")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length")
+    ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--label", default="decode_step")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--bench-json", help="the line an unprofiled run of the same command printed")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.label, args.command, args.bench_json)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.command)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -75,11 +113,9 @@ def main():
     import torch
 
     import attention_page_table_amd as tf
-    from synth.configs import decode_batch, prefill_chunk
-    from synth.device import alloc_pool, populate, query_inputs, write_rows  # noqa: F401
-    from synth.device import fill_bf16, _rid
     from synth import TAG_LATENT, TAG_PKEY
-    from synth.configs import LAT, ROPE, ROW
+    from synth.configs import LAT, ROPE, ROW, decode_batch, prefill_chunk
+    from synth.device import _rid, alloc_pool, fill_bf16, populate, query_inputs
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     tf.lib()  # fails loudly when the HIP library is missing
@@ -90,11 +126,8 @@ def main():
     log(f"setup: {wl.name}: pool {wl.n_pages} pages x {plan.page_bytes} B, {args.replicas} copies")
     P0 = alloc_pool(wl, plan)
     populate(P0)
-    pools = [P0.pool]
-    for _ in range(args.replicas - 1):
-        pools.append(P0.pool.clone())
-    pt = P0.pt
-    views = [tf.view(p, pt, wl.pt_stride, wl.n_pages) for p in pools]
+    pools = [P0.pool] + [P0.pool.clone() for _ in range(args.replicas - 1)]
+    views = [tf.view(p, P0.pt, wl.pt_stride, wl.n_pages) for p in pools]
     rows = wl.rows
     R = len(rows)
     rs, rp, iq, w, q = query_inputs(wl, 0, rows)
@@ -114,116 +147,115 @@ def main():
     blocks = torch.empty((R, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
-    ws_topk = torch.empty(max(1, tf.topk_workspace_bytes(R, ld, wl.k)), dtype=torch.uint8, device="cuda")
-    ws_attn = torch.empty(max(1, tf.attn_workspace_bytes(R, wl.Hq, wl.k)), dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(576.0)
     torch.cuda.synchronize()
 
     names = ["write", "indexer", "topk", "attention"]
+    launches = []
+    for v in views:
+        launches.append([
+            tf.latent_write(plan, v, rs, rp, lat_new, rope_new, pkey_stream=rs, pkey_idx=kidx, pkeys=key_new,
+                            prepare=True),
+            tf.indexer_logits(plan, v, rs, rp, iq, w, logits, n_valid=nv, prepare=True),
+            tf.topk_blocks(logits, nv, wl.k, blocks, prepare=True),
+            tf.sparse_mla_attn(plan, v, rs, rp, q, scale, blocks, out, lse, prepare=True),
+        ])
 
-    def step(i, ev=None):
-        v = views[i % len(views)]
-        if ev is not None:
-            ev[0].record()
-        tf.latent_write(plan, v, rs, rp, lat_new, rope_new, pkey_stream=rs, pkey_idx=kidx, pkeys=key_new)
-        if ev is not None:
-            ev[1].record()
-        tf.indexer_logits(plan, v, rs, rp, iq, w, logits, n_valid=nv)
-        if ev is not None:
-            ev[2].record()
-        tf.topk_blocks(logits, nv, wl.k, blocks, ws=ws_topk)
-        if ev is not None:
-            ev[3].record()
-        tf.sparse_mla_attn(plan, v, rs, rp, q, scale, blocks, out, lse, ws=ws_attn)
-        if ev is not None:
-            ev[4].record()
-
-    def run(i, timing=False):
-        step(i, evs[i] if timing else None)
-
-    # warmup
-    evs = None
     for i in range(args.warmup):
-        run(i)
+        for f in launches[i % len(launches)]:
+            f()
+    # calibration stream for the HBM byte counters (outside the timed region)
+    cal_src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    torch.neg(cal_src, out=cal_dst)
+    del cal_src, cal_dst
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
+    # ------------------------------------------------------------------ timed region: exactly K steps
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    per_kernel = {n: [] for n in names}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
     for i in range(K):
-        run(i, timing=True)
+        ev, ls = evs[i], launches[i % len(launches)]
+        ev[0].record()
+        ls[0]()
+        ev[1].record()
+        ls[1]()
+        ev[2].record()
+        ls[2]()
+        ev[3].record()
+        ls[3]()
+        ev[4].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / K
-    for i in range(K):
-        for j, n in enumerate(names):
-            per_kernel[n].append(evs[i][j].elapsed_time(evs[i][j + 1]))
+    ms_per_step = t_start.elapsed_time(t_end) / K
+    per_kernel = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)] for j, n in enumerate(names)}
     avg_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
 
     lat_bytes = R * wl.k * 4 * ROW_BYTES                       # selected latent + rope rows
-    value = lat_bytes / (ms_per_step * 1e-3) / 1e9
+    key_bytes = R * ld * wl.Dk * 2                             # every visible pooled key (all rows see ld)
     alg_bytes = {
-        "write": R * (ROW_BYTES + wl.Dk * 2) * 2,
-        "indexer": R * ld * (wl.Dk * 2 + 4) + R * wl.H * (wl.Dk * 2 + 4),
-        "topk": R * ld * 4 + R * wl.k * 4,
-        "attention": lat_bytes + R * wl.Hq * 576 * 2 + R * wl.Hq * 512 * 4 + R * wl.k * 4,
+        "write": R * (ROW_BYTES + wl.Dk * 2) * 2 + R * 16,
+        "indexer": key_bytes + R * ld * 4 + R * wl.H * (wl.Dk * 2 + 4) + R * 12,
+        "topk": R * ld * 4 + R * wl.k * 4 + R * 4,
+        "attention": lat_bytes + R * wl.Hq * 576 * 2 + R * wl.Hq * (512 + 1) * 4 + R * wl.k * 4 + R * 8,
     }
-    kern = {n: {"us": avg_ms[n] * 1e3, "alg_bytes": alg_bytes[n],
-                "GBps": alg_bytes[n] / (avg_ms[n] * 1e-3) / 1e9 if avg_ms[n] > 0 else None}
-            for n in names}
+    value = (lat_bytes + key_bytes) / (ms_per_step * 1e-3) / 1e9
+    kern = {n: {"us": round(avg_ms[n] * 1e3, 3), "alg_bytes": alg_bytes[n],
+                "GBps": round(alg_bytes[n] / (avg_ms[n] * 1e-3) / 1e9, 1)} for n in names}
     dom = max(["indexer", "topk", "attention"], key=lambda n: avg_ms[n])
-    src = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "attention.hip"}[dom]
-    traffic = load_traffic(dom, os.path.join(ROOT, "attention_page_table_amd", "csrc", src))
-    achieved = kern[dom]["GBps"]
+    achieved = alg_bytes[dom] / (avg_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                "alg_bytes_per_launch": alg_bytes[dom], "avg_launch_us": round(avg_ms[dom] * 1e3, 2)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
+                "kernel": f"tf_{'sparse_mla_attn' if dom == 'attention' else dom}",
+                "launches": list(ENTRIES[dom][0]), "alg_bytes_per_launch": alg_bytes[dom],
+                "avg_launch_us": round(avg_ms[dom] * 1e3, 2)}
 
     # ------------------------------------------------------------------ prefill indexer
     prefill = None
     if not args.no_prefill:
+        del launches, views, pools, P0
+        torch.cuda.empty_cache()
         pw = prefill_chunk(0)
         pplan = tf.kv_pool_plan(tf.geom(1, pw.Dk))
         log(f"setup: {pw.name}")
         PP = alloc_pool(pw, pplan)
         populate(PP)
         prs, prp, piq, pww, _ = query_inputs(pw, 0, pw.rows)
-        pld = 25000
+        pld = (pw.rows[-1][1]) // 4 + 1
         plog = torch.empty((len(pw.rows), pld), dtype=torch.float32, device="cuda")
         pnv = torch.empty(len(pw.rows), dtype=torch.int32, device="cuda")
-        pv = PP.view()
+        f = tf.indexer_logits(pplan, PP.view(), prs, prp, piq, pww, plog, n_valid=pnv, prepare=True)
         for _ in range(3):
-            tf.indexer_logits(pplan, pv, prs, prp, piq, pww, plog, n_valid=pnv)
+            f()
         torch.cuda.synchronize()
         reps = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            tf.indexer_logits(pplan, pv, prs, prp, piq, pww, plog, n_valid=pnv)
-        e1.record()
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        pe[0].record()
+        for i in range(reps):
+            f()
+            pe[i + 1].record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = float(np.mean([pe[i].elapsed_time(pe[i + 1]) for i in range(reps)])) * 1e3
         flops = sum(2 * pw.H * pw.Dk * (t // 4 + 1) for _, t in pw.rows)
         tfl = flops / (us * 1e-6) / 1e12
-        prefill = {"kernel": "indexer", "workload": pw.name, "us": round(us, 2), "causal_flop": flops,
+        prefill = {"call": "tf_indexer_logits", "launches": list(ENTRIES["indexer_prefill"][0]),
+                   "workload": pw.name, "rows": len(pw.rows), "keys": pld, "us": round(us, 2),
+                   "causal_flop": flops,
                    "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
-                                "traffic": load_traffic("indexer_prefill", os.path.join(
-                                    ROOT, "attention_page_table_amd", "csrc", "indexer.hip"))}}
+                                "traffic": load_traffic("indexer_prefill")}}
         del PP, plog
 
     # ------------------------------------------------------------------ oracle on the host
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, rows, ld, scale, args.cpu_reps, lat_bytes)
+        cpu = cpu_baseline(wl, rows, ld, scale, args.cpu_seconds, lat_bytes + key_bytes)
 
     line = {
         "metric": "paged DSA decode: latent GB/s (% HBM peak); prefill chunk indexer % MFMA peak",
@@ -232,12 +264,11 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "streams": R, "context": wl.lengths[0], "caches": 1,
                    "attn_heads": wl.Hq, "indexer_heads": wl.H, "index_dim": wl.Dk, "topk_blocks": wl.k,
-                   "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": len(views),
-                   "launches": "eager, one HIP event between kernels"},
+                   "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": args.replicas,
+                   "value_bytes_per_step": lat_bytes + key_bytes,
+                   "launches": "eager, marshalled once, one HIP event between calls"},
         "roofline": roofline,
-        "kernels": {n: {k2: (round(v2, 3) if isinstance(v2, float) else v2) for k2, v2 in d.items()}
-                    for n, d in kern.items()},
-        "attention_latent_GBps": round(lat_bytes / (avg_ms["attention"] * 1e-3) / 1e9, 1),
+        "kernels": kern,
         "prefill_indexer": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
@@ -245,13 +276,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, rows, ld, scale, reps, lat_bytes):
+def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
     """The oracle (fp64 numpy) on the same decode step: logits over every pooled
-    key, exact top-k, attention over the selected rows. Inputs are generated before
-    timing; only the oracle's arithmetic is timed."""
+    key, exact top-k, attention over the selected rows, repeated for about
+    `seconds`. Inputs are generated before timing; only the oracle's arithmetic is
+    timed."""
     import numpy as np
     from oracle import indexer_logits, sparse_mla, topk_blocks
     from oracle import workload as ow
+    from oracle.attention import selected_tokens
     from synth import bf16_to_f64
     try:
         from threadpoolctl import threadpool_info
@@ -264,31 +297,31 @@ def cpu_baseline(wl, rows, ld, scale, reps, lat_bytes):
     keys = [ow.keys_of(wl, 0, b, t // 4 + 1) for b, t in rows]
     q_a = bf16_to_f64(wl.q_bits(0, rows))
     pos = [t for _, t in rows]
-    t_idx = []
-    t_att = []
-    for _ in range(reps):
+    lg = indexer_logits(q_i, w_i, keys, pos, ld)
+    blk = topk_blocks(lg, [min(t // 4 + 1, ld) for t in pos], wl.k)
+    cache = {}
+    for r, (b, t) in enumerate(rows):                 # the selected rows (generator work, untimed)
+        S = selected_tokens(blk[r], t)
+        cache[r] = dict(zip(S.tolist(), range(S.size))), ow.rows_reader(wl, 0, b)(S)
+
+    def rows_of(r, S):
+        m, (lat, rope) = cache[r]
+        ix = [m[s] for s in S.tolist()]
+        return lat[ix], rope[ix]
+
+    steps, busy = 0, 0.0
+    while busy < seconds:
         t0 = time.perf_counter()
         lg = indexer_logits(q_i, w_i, keys, pos, ld)
         blk = topk_blocks(lg, [min(t // 4 + 1, ld) for t in pos], wl.k)
-        t_idx.append(time.perf_counter() - t0)
-        # gather the selected rows (generator work, untimed), then time the attention
-        from oracle.attention import selected_tokens
-        cache = {}
-        for r, (b, t) in enumerate(rows):
-            S = selected_tokens(blk[r], t)
-            cache[r] = dict(zip(S.tolist(), range(S.size))), ow.rows_reader(wl, 0, b)(S)
-        def rows_of(r, S):
-            m, (lat, rope) = cache[r]
-            ix = [m[s] for s in S.tolist()]
-            return lat[ix], rope[ix]
-        t0 = time.perf_counter()
         sparse_mla(q_a, rows_of, blk, pos, scale)
-        t_att.append(time.perf_counter() - t0)
-    sec = float(np.median(t_idx) + np.median(t_att))
-    return {"value": round(lat_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole decode step ({len(rows)} rows: logits over {ld} keys each, top-{wl.k}, "
-                      f"attention), median of {reps}", "seconds_per_step": round(sec, 4),
-            "cpu_model": _cpu_model()}
+        busy += time.perf_counter() - t0
+        steps += 1
+    sec = busy / steps
+    return {"value": round(step_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole decode steps of the same workload ({len(rows)} rows: logits over {ld} "
+                      f"keys each, exact top-{wl.k}, attention over the selected rows), {busy:.1f} s",
+            "seconds_per_step": round(sec, 4), "cpu_model": _cpu_model()}
 
 
 def _cpu_model():
@@ -299,6 +332,118 @@ def _cpu_model():
     except Exception:
         pass
     return None
+
+
+# ---------------------------------------------------------------------- profile summaries
+def _entry_of(name):
+    for e, (prefixes, _) in ENTRIES.items():
+        if any(name.startswith(p) or name.startswith("void " + p) for p in prefixes):
+            return e
+    return None
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_trace(db, label, command, bench_json=None):
+    """Per-kernel durations from a rocprofv3 --kernel-trace database, written to
+    profiles/<label>.txt, with the command that produced it; with `bench_json`, the
+    HIP-event durations an unprofiled run of the same command measured beside them
+    (the tracer itself lengthens the gaps between launches, not the kernels)."""
+    c = sqlite3.connect(db)
+    stats, grids = {}, {}
+    rows = c.execute("select name, start, end, grid_x * grid_y * grid_z from kernels").fetchall()
+    for name, _, _, g in rows:
+        grids.setdefault(_short(name), set()).add(g)
+    for name, start, end, g in rows:   # a kernel launched at several grid sizes gets a line per size
+        n = _short(name)
+        key = f"{n} [grid {g}]" if len(grids[n]) > 1 else n
+        stats.setdefault(key, []).append((end - start) / 1000.0)
+    lines = [f"# rocprofv3 kernel trace: {label}", f"# command: {command}", "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_us':>12s}"]
+    per_entry = {}
+    for n, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{n[:60]:60s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} {max(v):10.2f} "
+                     f"{sum(v):12.1f}")
+        e = _entry_of(n)
+        if e is not None:
+            per_entry.setdefault(e, []).append((n, len(v), sum(v) / len(v)))
+    # an entry's kernel launched at several sizes: keep the size launched most often (the timed one)
+    for e, ks in per_entry.items():
+        best = {}
+        for n, cnt, a in ks:
+            base = n.split(" [grid")[0]
+            if base not in best or cnt > best[base][1]:
+                best[base] = (n, cnt, a)
+        per_entry[e] = list(best.values())
+    lines += ["", "# per entry point: sum of its kernels' average durations (one launch each per call)"]
+    for e, ks in per_entry.items():
+        lines.append(f"{e:16s} {sum(a for _, _, a in ks):10.2f} us  <- " + " + ".join(
+            f"{n} ({a:.2f})" for n, _, a in ks))
+    if bench_json:
+        b = json.loads([ln for ln in open(bench_json) if ln.startswith("{")][-1])
+        lines += ["", "# HIP events in an unprofiled run of the same command (launch to launch, so each also holds"
+                      " one dispatch gap) vs the kernels' own durations above"]
+        ev = {n: d["us"] for n, d in b["kernels"].items()}
+        if b.get("prefill_indexer"):
+            ev["indexer_prefill"] = b["prefill_indexer"]["us"]
+        for e, us in ev.items():
+            k = sum(a for _, _, a in per_entry.get(e, []))
+            lines.append(f"{e:16s} events {us:9.2f} us   kernels {k:9.2f} us   ratio {us / k if k else 0:.3f}")
+        lines.append(f"dominant call: {b['roofline']['kernel']}  achieved {b['roofline']['achieved']} GB/s "
+                     f"= {b['roofline']['alg_bytes_per_launch']} B / {b['roofline']['avg_launch_us']} us")
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"{label}.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc(db, counter):
+    """kernel -> counter values per dispatch, for the grid size launched most often
+    (the timed launches, not the pool population's)."""
+    c = sqlite3.connect(db)
+    by = {}
+    for name, g, v in c.execute("select p.name, k.grid_x * k.grid_y * k.grid_z, p.counter_value from pmc_events p "
+                                "join kernels k on p.dispatch_id = k.dispatch_id where p.counter_name = ?",
+                                (counter,)):
+        by.setdefault(_short(name), {}).setdefault(g, []).append(float(v))
+    counts = [len(v) for n, gs in by.items() if _entry_of(n) for v in gs.values()]
+    timed = max(set(counts), key=counts.count)       # the decode step's launch count
+    return {n: next((v for v in gs.values() if len(v) == timed), max(gs.values(), key=len)) for n, gs in by.items()}
+
+
+def summarize_pmc(fetch_db, write_db, command):
+    """HBM bytes per launch of each entry point from one FETCH_SIZE and one WRITE_SIZE
+    pass (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration stream (CAL_BYTES read and CAL_BYTES written by one torch.neg)."""
+    fetch, write = _pmc(fetch_db, "FETCH_SIZE"), _pmc(write_db, "WRITE_SIZE")
+    cal = [k for k in fetch if CAL_KERNEL in k]
+    assert cal, "the calibration kernel is missing from the FETCH_SIZE pass"
+    cf = CAL_BYTES / (fetch[cal[0]][0] * 1024.0)
+    cw = CAL_BYTES / (write[[k for k in write if CAL_KERNEL in k][0]][0] * 1024.0)
+    entries = {}
+    for n in fetch:
+        e = _entry_of(n)
+        if e is None:
+            continue
+        f_kib = sum(fetch[n]) / len(fetch[n])
+        w_kib = sum(write.get(n, [0.0])) / max(1, len(write.get(n, [])))
+        d = entries.setdefault(e, {"kernels": {}, "source_sha256_16": source_hash(ENTRIES[e][1])})
+        d["kernels"][n] = {"fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1), "dispatches": len(fetch[n])}
+    for e, d in entries.items():
+        fb = sum(k["fetch_kib"] for k in d["kernels"].values()) * 1024.0 * cf
+        wb = sum(k["write_kib"] for k in d["kernels"].values()) * 1024.0 * cw
+        d["fetch_bytes_per_launch"] = round(fb)
+        d["write_bytes_per_launch"] = round(wb)
+        d["hbm_bytes_per_launch"] = round(fb + wb)
+    res = {"command": command, "calibration": {"kernel": cal[0], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES,
+                                               "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)},
+           "entries": entries}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, TRAFFIC_FILE)
+    json.dump(res, open(path, "w"), indent=1)
+    print(json.dumps(res, indent=1))
 
 
 if __name__ == "__main__":
