@@ -89,20 +89,27 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
       for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
     }
   };
-  bf16x8 cur[KS], nxt[KS];
-  if (kb < kend) load(kb, cur);
-  for (int64_t kt = kb; kt < kend; kt += 32) {
-    if (kt + 32 < kend) load(kt + 32, nxt);
+  // three subtiles in flight: slot s holds subtile kb + 32 (3i + s)
+  auto step = [&](int64_t kt, bf16x8 (&cur)[KS]) {
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], cur[ks], acc, 0, 0, 0);
+    const int pg = page_at(kt);
+    if (kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < H; ++i) s = __builtin_fmaf(wv[i], __builtin_fmaxf(acc[i], 0.f), s);
     const int64_t key = kt + n;
-    if (g == 0 && key < ke) out[key] = key < nc ? (page_at(kt) >= 0 ? s : __builtin_nanf("")) : ninf;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+    if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
+  };
+  bf16x8 s0[KS], s1[KS], s2[KS];
+  if (kb < kend) load(kb, s0);
+  if (kb + 32 < kend) load(kb + 32, s1);
+  if (kb + 64 < kend) load(kb + 64, s2);
+  for (int64_t kt = kb; kt < kend; kt += 96) {
+    step(kt, s0);
+    if (kt + 32 < kend) step(kt + 32, s1);
+    if (kt + 64 < kend) step(kt + 64, s2);
   }
   // keys past the compressed length
   for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) out[key] = ninf;
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
 // ---- tile path -----------------------------------------------------------------------------
 template <int D>
 struct KeyTile {
-  __bf16 k[2][32 * D];   // two 32-key subtiles, 16-byte chunks swizzled by key
+  __bf16 k[32 * D];   // one 32-key subtile, 16-byte chunks swizzled by key
 };
 
 // Swizzled position of chunk c of key j in a subtile (chunks of 16 bytes, CH per key).
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   constexpr int CH = D / 8;     // 16-byte chunks per key
   constexpr int ROWS = 4 * MT * RPT;
   constexpr int kMaxPages = 40;
-  __shared__ KeyTile<D> kt_lds;
+  __shared__ KeyTile<D> kt_lds0, kt_lds1;
   __shared__ int32_t pg_lds[kMaxPages];
   __shared__ int32_t uniform_flag;
 
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 
   // global -> LDS loads of one subtile: CH*32 chunks, 64 per wave-wide load; the lane
   // that fills swizzled position p loads the chunk that belongs there.
-  auto issue = [&](int64_t kt, int buf) {
+  auto issue = [&](int64_t kt, __bf16* dst) {
     const int pg = pg_lds[(int)(kt / kKeysPerPage) - p0];
     for (int i = wave; i < CH * 32 / 64; i += 4) {
       const int p = i * 64 + lane;           // swizzled position
@@ -230,14 +237,14 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
       const char* src = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey +
                                       (int64_t)((kt % kKeysPerPage) + j) * a.pkey_row_bytes + c * 16
                                 : a.v.pool + c * 16;   // any readable bytes: rows of a missing page become NaN
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&kt_lds.k[buf][i * 64 * 8], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&dst[i * 64 * 8], 16, 0, 0);
     }
   };
 
   const float ninf = -__builtin_inff();
   const float qnan = __builtin_nanf("");
-  // a subtile's scores are stored one iteration late, so the barrier that waits for
-  // the next subtile's keys does not also wait for fresh stores
+  // a subtile's scores are stored one iteration late, after the next subtile's loads
+  // are issued
   float pend[MT][RH];
   int64_t pend_kt = -1;
   auto flush = [&]() {
@@ -249,16 +256,10 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 #pragma unroll
       for (int r = 0; r < RH; ++r) a.logits[(int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ld + key] = pend[t][r];
   };
-  int buf = 0;
-  if (kb < kend) issue(kb, 0);
-  for (int64_t kt = kb; kt < kend; kt += 32) {
-    __syncthreads();   // this subtile has landed; the other buffer is free
-    if (kt + 32 < kend) issue(kt + 32, buf ^ 1);
-    flush();
+  auto compute = [&](int64_t kt, const __bf16* src) {
     bf16x8 bfrag[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bfrag[ks] = *(const bf16x8*)&kt_lds.k[buf][swz<CH>(n, 2 * ks + g) * 8];
+    for (int ks = 0; ks < KS; ++ks) bfrag[ks] = *(const bf16x8*)&src[swz<CH>(n, 2 * ks + g) * 8];
     __builtin_amdgcn_sched_barrier(0);
     const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
     const int64_t key = kt + n;
@@ -276,7 +277,24 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
       }
     }
     pend_kt = kt;
-    buf ^= 1;
+  };
+  // Two LDS buffers (distinct arrays, so the compiler sees that a subtile's reads
+  // and the next subtile's loads touch different memory). Each wave waits for its
+  // own loads of a subtile just before the barrier that publishes it, so the loads
+  // of the next subtile overlap this one's MFMAs.
+  if (kb < kend) issue(kb, kt_lds0.k);
+  for (int64_t kt = kb; kt < kend; kt += 64) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of subtile kt
+    __syncthreads();                      // ... and every other wave's; buffer 1 is free
+    if (kt + 32 < kend) issue(kt + 32, kt_lds1.k);
+    flush();
+    compute(kt, kt_lds0.k);
+    if (kt + 32 >= kend) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (kt + 64 < kend) issue(kt + 64, kt_lds0.k);
+    flush();
+    compute(kt + 32, kt_lds1.k);
   }
   flush();
   // keys past every row's compressed length

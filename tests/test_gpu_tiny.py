@@ -231,6 +231,52 @@ def test_topk_edge_cases():
     assert np.array_equal(host(blk), np.tile(np.arange(512), (2, 1)))
 
 
+def test_topk_blocked_workspace_reuse_and_graph_replay():
+    """Long rows merge per-block candidates through the workspace: a reused workspace,
+    a workspace of arbitrary bytes and replays of a captured call all give the exact
+    top-k."""
+    _log("top-k blocked mode: workspace reuse, arbitrary workspace bytes, graph replays")
+    rng = np.random.default_rng(9)
+    R, ld, k = 5, 33000, 512
+    nv = np.array([ld, 30000, 4097, 513, 20000], dtype=np.int32)
+    vals = [rng.standard_normal((R, ld)).astype(np.float32) for _ in range(3)]
+    want = [topk_on_values(v, nv, k) for v in vals]
+    nvt = torch.from_numpy(nv).cuda()
+    need = tf.topk_workspace_bytes(R, ld, k)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    lg = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    blk = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    for i in range(6):                                   # the same workspace, call after call
+        lg.copy_(torch.from_numpy(vals[i % 3]))
+        tf.topk_blocks(lg, nvt, k, blk, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(blk), want[i % 3]), f"reuse {i}"
+    junk = torch.from_numpy(rng.integers(0, 256, size=need, dtype=np.uint8)).cuda()
+    tf.topk_blocks(lg, nvt, k, blk, ws=junk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(blk), want[5 % 3]), "arbitrary workspace bytes"
+    # one captured launch (one epoch) replayed with eager calls on the same workspace between
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            tf.topk_blocks(lg, nvt, k, blk, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(6):
+        lg.copy_(torch.from_numpy(vals[i % 3]))
+        blk.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(blk), want[i % 3]), f"replay {i}"
+        if i % 2 == 1:                                   # eager work between replays
+            tf.topk_blocks(lg, nvt, k, blk, ws=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(blk), want[i % 3]), f"eager after replay {i}"
+
+
 def test_empty_and_degenerate(tiny_pool):
     _log("degenerate calls: zero rows, blocks all -1")
     wl, plan, P = tiny_pool
