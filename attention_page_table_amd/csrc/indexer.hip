@@ -21,6 +21,8 @@
 //  * row kernel (few rows of distinct streams, e.g. a decode batch; HBM-bound): each
 //    wave streams one row's keys straight into B fragments, one subtile ahead, with
 //    the row's page ids preloaded across the lanes.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tf {
@@ -42,6 +44,11 @@ struct IdxArgs {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// max(x, 0) as one v_med3_f32 (the median of x, 0 and +inf). fmaxf would first
+// quiet a signaling NaN with one more instruction per value; here a NaN gives 0
+// either way.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); }
 
 __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
   const int pos = a.row_pos[row];
@@ -98,7 +105,7 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
     if (kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < H; ++i) s = __builtin_fmaf(wv[i], __builtin_fmaxf(acc[i], 0.f), s);
+    for (int i = 0; i < H; ++i) s = __builtin_fmaf(wv[i], relu(acc[i]), s);
     const int64_t key = kt + n;
     if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
   };
@@ -134,9 +141,11 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
 }
 
 // ---- tile path -----------------------------------------------------------------------------
+constexpr int kChunk = 128;   // keys per LDS chunk: one page's pooled keys
+
 template <int D>
-struct KeyTile {
-  __bf16 k[32 * D];   // one 32-key subtile, 16-byte chunks swizzled by key
+struct KeyChunk {
+  __bf16 k[kChunk * D];   // four 32-key subtiles; within each, 16-byte pieces swizzled by key
 };
 
 // Swizzled position of chunk c of key j in a subtile (chunks of 16 bytes, CH per key).
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   constexpr int CH = D / 8;     // 16-byte chunks per key
   constexpr int ROWS = 4 * MT * RPT;
   constexpr int kMaxPages = 40;
-  __shared__ KeyTile<D> kt_lds0, kt_lds1;
+  __shared__ KeyChunk<D> kc0, kc1;
   __shared__ int32_t pg_lds[kMaxPages];
   __shared__ int32_t uniform_flag;
 
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   }
 
   // largest compressed length of the workgroup's rows: keys past it are -inf only
-  int nc_max = 0;
+  int nc_max = 0, nc_min = 0x7fffffff;
   int rnc[MT][RH];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -197,6 +206,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   for (int rr = 0; rr < ROWS; ++rr) {
     const int c = nc_of(a, row_base + rr);
     nc_max = c > nc_max ? c : nc_max;
+    nc_min = c < nc_min ? c : nc_min;
   }
   const int64_t kend = ke < nc_max ? ke : nc_max;
 
@@ -220,49 +230,59 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
         afrag[t][ks] = *(const bf16x8*)(a.q + ((int64_t)row * H + head) * D + ks * 16 + g * 8);
     }
   }
+  // weights of the (row, head) pairs of this lane's accumulators
   float wv[MT][16];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) wv[t][i] = a.w[(int64_t)(wave_row0 + t * RPT + g * RH + i / H) * H + (i % H)];
+  // this lane's output rows, at key n
+  float* optr[MT][RH];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < RH; ++r) optr[t][r] = a.logits + (int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ld + n;
   __syncthreads();
 
-  // global -> LDS loads of one subtile: CH*32 chunks, 64 per wave-wide load; the lane
-  // that fills swizzled position p loads the chunk that belongs there.
-  auto issue = [&](int64_t kt, __bf16* dst) {
+  // global -> LDS loads of one 128-key chunk (one page, since kb is a multiple of
+  // 128): 32 * CH pieces of 16 bytes per subtile, 64 per wave-wide load; the lane that
+  // fills swizzled position p loads the piece that belongs there. Keys past kend in
+  // the chunk are read too (same page) and masked when scored.
+  auto issue = [&](int64_t kt, __bf16* dst) __attribute__((always_inline)) {
     const int pg = pg_lds[(int)(kt / kKeysPerPage) - p0];
-    for (int i = wave; i < CH * 32 / 64; i += 4) {
-      const int p = i * 64 + lane;           // swizzled position
-      const int j = p / CH, c = (p % CH) ^ (j & (CH - 1));
-      const char* src = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey +
-                                      (int64_t)((kt % kKeysPerPage) + j) * a.pkey_row_bytes + c * 16
-                                : a.v.pool + c * 16;   // any readable bytes: rows of a missing page become NaN
+    const char* base = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey : nullptr;
+#pragma unroll
+    for (int i = wave; i < CH * kChunk / 64; i += 4) {
+      const int p = i * 64 + lane;
+      const int sub = p / (CH * 32), q = p % (CH * 32);
+      const int j = q / CH, c = (q % CH) ^ (j & (CH - 1));
+      const char* src = base ? base + (int64_t)(sub * 32 + j) * a.pkey_row_bytes + c * 16
+                             : a.v.pool + c * 16;   // any readable bytes: rows of a missing page become NaN
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&dst[i * 64 * 8], 16, 0, 0);
     }
   };
 
   const float ninf = -__builtin_inff();
   const float qnan = __builtin_nanf("");
-  // a subtile's scores are stored one iteration late, after the next subtile's loads
-  // are issued
-  float pend[MT][RH];
-  int64_t pend_kt = -1;
-  auto flush = [&]() {
-    if (pend_kt < 0) return;
-    const int64_t key = pend_kt + n;
-    if (key >= ke) return;
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < RH; ++r) a.logits[(int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ld + key] = pend[t][r];
-  };
-  auto compute = [&](int64_t kt, const __bf16* src) {
+  // One 32-key subtile: B fragments from LDS, MT x KS MFMAs, the head sum, the
+  // stores. Subtiles past kend are computed too (their keys are in the chunk's page)
+  // and only keys < ke are stored. Modes: kOpen, every key of the chunk is stored
+  // and visible to every row (no selects); kFull, every key is stored; kPart, keys
+  // are tested against ke.
+  constexpr int kOpen = 0, kFull = 1, kPart = 2;
+  auto subtile = [&](int64_t kt, const __bf16* src, bool pg_ok, auto mode) __attribute__((always_inline)) {
+    constexpr int M = decltype(mode)::value;
     bf16x8 bfrag[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bfrag[ks] = *(const bf16x8*)&src[swz<CH>(n, 2 * ks + g) * 8];
-    __builtin_amdgcn_sched_barrier(0);
-    const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
     const int64_t key = kt + n;
+    // B reads interleaved with the first MFMAs: four reads, then one read per two MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
+#pragma unroll
+    for (int i = 0; i < KS / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       f32x16 acc = {};
@@ -272,31 +292,66 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
       for (int r = 0; r < RH; ++r) {
         float s = 0.f;
 #pragma unroll
-        for (int h = 0; h < H; ++h) s = __builtin_fmaf(wv[t][r * H + h], __builtin_fmaxf(acc[r * H + h], 0.f), s);
-        pend[t][r] = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
+        for (int h = 0; h < H; ++h) s = __builtin_fmaf(wv[t][r * H + h], relu(acc[r * H + h]), s);
+        if (M == kOpen) {
+          optr[t][r][kt] = s;
+        } else {
+          const float v = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
+          if (M == kFull || key < ke) optr[t][r][kt] = v;
+        }
       }
     }
-    pend_kt = kt;
   };
-  // Two LDS buffers (distinct arrays, so the compiler sees that a subtile's reads
-  // and the next subtile's loads touch different memory). Each wave waits for its
-  // own loads of a subtile just before the barrier that publishes it, so the loads
-  // of the next subtile overlap this one's MFMAs.
-  if (kb < kend) issue(kb, kt_lds0.k);
-  for (int64_t kt = kb; kt < kend; kt += 64) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of subtile kt
-    __syncthreads();                      // ... and every other wave's; buffer 1 is free
-    if (kt + 32 < kend) issue(kt + 32, kt_lds1.k);
-    flush();
-    compute(kt, kt_lds0.k);
-    if (kt + 32 >= kend) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+  // which mode a chunk runs in, and the vector-memory operations it issues after the
+  // next chunk's loads (its stores), so that the next barrier waits for the loads only
+  auto chunk = [&](int64_t kt, const __bf16* src) __attribute__((always_inline)) -> bool {
+    const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
+    if (kt + kChunk <= ke && pg_ok && kt + kChunk <= nc_min) {
+#pragma unroll
+      for (int sub = 0; sub < kChunk / 32; ++sub)
+        subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kOpen>{});
+      return true;
+    }
+    if (kt + kChunk <= ke) {
+#pragma unroll
+      for (int sub = 0; sub < kChunk / 32; ++sub)
+        subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kFull>{});
+      return true;
+    }
+#pragma unroll
+    for (int sub = 0; sub < kChunk / 32; ++sub)
+      subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kPart>{});
+    return false;
+  };
+  // Wait for this wave's loads of the chunk about to be published. After a chunk
+  // that stored every key (a fixed number of stores, issued after the loads), the
+  // stores may stay in flight: vector-memory operations complete in issue order.
+  constexpr int kStores = (kChunk / 32) * MT * RH;
+  static_assert(kStores < 64, "vmcnt holds at most 63");
+  // s_waitcnt immediate for vmcnt(N) alone (expcnt and lgkmcnt at their maxima)
+  constexpr int kWaitStores = (kStores & 15) | ((kStores >> 4) << 14) | 0x0F70;
+  auto wait_loads = [&](bool stores_fixed) __attribute__((always_inline)) {
+    if (stores_fixed) __builtin_amdgcn_s_waitcnt(kWaitStores);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  };
+  // Two LDS chunks (distinct arrays, so the compiler sees that a chunk's reads and
+  // the next chunk's loads touch different memory). Each wave waits for its own
+  // loads of a chunk just before the barrier that publishes it, so the loads of the
+  // next chunk overlap this one's MFMAs.
+  if (kb < kend) issue(kb, kc0.k);
+  bool fixed = false;   // nothing but the first chunk's loads in flight
+  for (int64_t kt = kb; kt < kend; kt += 2 * kChunk) {
+    wait_loads(fixed);
+    __syncthreads();   // every wave's loads of chunk kt have landed; the other chunk is free
+    if (kt + kChunk < kend) issue(kt + kChunk, kc1.k);
+    fixed = chunk(kt, kc0.k) && kt + kChunk < kend;
+    if (kt + kChunk >= kend) break;
+    wait_loads(fixed);
     __syncthreads();
-    if (kt + 64 < kend) issue(kt + 64, kt_lds0.k);
-    flush();
-    compute(kt + 32, kt_lds1.k);
+    if (kt + 2 * kChunk < kend) issue(kt + 2 * kChunk, kc0.k);
+    fixed = chunk(kt + kChunk, kc1.k) && kt + 2 * kChunk < kend;
   }
-  flush();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   // keys past every row's compressed length
   const int64_t kf = kend > kb ? kend : kb;
   for (int rr = wave; rr < ROWS; rr += 4)
@@ -310,8 +365,8 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
     constexpr int MT = 2;
     constexpr int ROWS = 4 * MT * RPT;
     const int64_t rgroups = (n_rows + ROWS - 1) / ROWS;
-    // about 2,048 workgroups, each over a multiple of 128 keys (at most 4,096)
-    int64_t kpw = (a.ld * rgroups + 2047) / 2048;
+    // about 1,024 workgroups (four per CU), each over a multiple of 128 keys (at most 4,096)
+    int64_t kpw = (a.ld * rgroups + 1023) / 1024;
     kpw = (kpw + 127) / 128 * 128;
     if (kpw < 128) kpw = 128;
     if (kpw > 4096) kpw = 4096;
