@@ -161,9 +161,27 @@ def main():
             tf.sparse_mla_attn(plan, v, rs, rp, q, scale, blocks, out, lse, prepare=True),
         ])
 
-    for i in range(args.warmup):
-        for f in launches[i % len(launches)]:
-            f()
+    # warmup; its last steps time every call (one HIP event between calls) to find the
+    # dominant call, which the timed region then brackets alone
+    W = max(args.warmup, 1)
+    n_probe = min(W, 10)
+    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_probe)]
+    for i in range(W):
+        ls = launches[i % len(launches)]
+        j = i - (W - n_probe)
+        if j >= 0:
+            wev[j][0].record()
+            for c in range(4):
+                ls[c]()
+                wev[j][c + 1].record()
+        else:
+            for f in ls:
+                f()
+    torch.cuda.synchronize()
+    warm_ms = {n: float(np.mean([wev[j][c].elapsed_time(wev[j][c + 1]) for j in range(n_probe)]))
+               for c, n in enumerate(names)}
+    dom = max(["indexer", "topk", "attention"], key=lambda n: warm_ms[n])
+    di = names.index(dom)
     # calibration stream for the HBM byte counters (outside the timed region)
     cal_src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
     cal_dst = torch.empty_like(cal_src)
@@ -173,7 +191,7 @@ def main():
 
     # ------------------------------------------------------------------ timed region: exactly K steps
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -181,21 +199,19 @@ def main():
     t_start.record()
     for i in range(K):
         ev, ls = evs[i], launches[i % len(launches)]
-        ev[0].record()
-        ls[0]()
-        ev[1].record()
-        ls[1]()
-        ev[2].record()
-        ls[2]()
-        ev[3].record()
-        ls[3]()
-        ev[4].record()
+        for c in range(4):
+            if c == di:
+                ev[0].record()
+                ls[c]()
+                ev[1].record()
+            else:
+                ls[c]()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = t_start.elapsed_time(t_end) / K
-    per_kernel = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)] for j, n in enumerate(names)}
-    avg_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    avg_ms = dict(warm_ms)
+    avg_ms[dom] = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]))
 
     lat_bytes = R * wl.k * 4 * ROW_BYTES                       # selected latent + rope rows
     key_bytes = R * ld * wl.Dk * 2                             # every visible pooled key (all rows see ld)
@@ -208,7 +224,6 @@ def main():
     value = (lat_bytes + key_bytes) / (ms_per_step * 1e-3) / 1e9
     kern = {n: {"us": round(avg_ms[n] * 1e3, 3), "alg_bytes": alg_bytes[n],
                 "GBps": round(alg_bytes[n] / (avg_ms[n] * 1e-3) / 1e9, 1)} for n in names}
-    dom = max(["indexer", "topk", "attention"], key=lambda n: avg_ms[n])
     achieved = alg_bytes[dom] / (avg_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
@@ -266,7 +281,8 @@ def main():
                    "attn_heads": wl.Hq, "indexer_heads": wl.H, "index_dim": wl.Dk, "topk_blocks": wl.k,
                    "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": args.replicas,
                    "value_bytes_per_step": lat_bytes + key_bytes,
-                   "launches": "eager, marshalled once, one HIP event between calls"},
+                   "launches": "eager, marshalled once; HIP events around the dominant call only",
+                   "kernels_timing": "dominant call: the timed region; the others: the last warmup steps"},
         "roofline": roofline,
         "kernels": kern,
         "prefill_indexer": prefill,
