@@ -49,83 +49,92 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// OR and AND of a value over the wave: within each row of 16 lanes by DPP, then the
+// four rows through readlane (the results are wave-uniform).
+__device__ __forceinline__ void wave_or_and(uint32_t& o, uint32_t& a) {
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0xB1, 0xf, 0xf, true);    // quad_perm [1,0,3,2]
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0xB1, 0xf, 0xf, true);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x4E, 0xf, 0xf, true);    // quad_perm [2,3,0,1]
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x4E, 0xf, 0xf, true);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x141, 0xf, 0xf, true);   // row_half_mirror
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x141, 0xf, 0xf, true);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x140, 0xf, 0xf, true);   // row_mirror
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x140, 0xf, 0xf, true);
+  o = __builtin_amdgcn_readlane(o, 0) | __builtin_amdgcn_readlane(o, 16) | __builtin_amdgcn_readlane(o, 32) |
+      __builtin_amdgcn_readlane(o, 48);
+  a = __builtin_amdgcn_readlane(a, 0) & __builtin_amdgcn_readlane(a, 16) & __builtin_amdgcn_readlane(a, 32) &
+      __builtin_amdgcn_readlane(a, 48);
+}
+
 struct SelShared {
-  uint32_t hist[kBins];
-  uint32_t wsum[kWaves];
-  uint32_t wgt[kWaves], weq[kWaves];
-  uint32_t bin, rem, orv, andv;
+  uint32_t hist[3][kBins];   // one histogram per radix pass, all cleared up front
+  uint32_t wor[kWaves], wand[kWaves], wsum[kWaves], wgt[kWaves], weq[kWaves];
+  uint32_t bin, rem;
 };
 
-// Exclusive prefix over the workgroup's threads; `total` receives the sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
-  if (lane == 63) wsum[wid] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s = wsum[w];
-    base += w < wid ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return base + x - v;
+// Exclusive prefix of the per-wave values v[0..kWaves) for this thread's wave, and
+// their total, from one LDS read per lane and a wave prefix sum.
+__device__ __forceinline__ uint32_t waves_before(const uint32_t* v, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t incl = wave_incl_scan(lane < kWaves ? v[lane] : 0u);
+  total = __builtin_amdgcn_readlane(incl, kWaves - 1);
+  return wid == 0 ? 0u : __builtin_amdgcn_readlane(incl, wid - 1);
 }
 
 // T = the k-th largest of the n > k valid keys (invalid slots hold 0, below every
-// valid key), rem = how many keys equal to T belong to the top k.
+// valid key), rem = how many keys equal to T belong to the top k. Three barriers per
+// radix pass: after the histogram, after the wave totals, after the selected bin.
 template <int E>
 __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uint32_t& T, uint32_t& rem) {
-  // common leading bits of the valid keys
-  uint32_t o = 0u, an = 0xFFFFFFFFu;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // common leading bits of the valid keys; clear the pass histograms
+  {
+    uint32_t o = 0u, an = 0xFFFFFFFFu;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] != 0u) {
-      o |= key[e];
-      an &= key[e];
+    for (int e = 0; e < E; ++e)
+      if (key[e] != 0u) {
+        o |= key[e];
+        an &= key[e];
+      }
+    wave_or_and(o, an);
+    if (lane == 0) {
+      sh.wor[wid] = o;
+      sh.wand[wid] = an;
     }
-  if (threadIdx.x == 0) {
-    sh.orv = 0u;
-    sh.andv = 0xFFFFFFFFu;
+    uint32_t* h = &sh.hist[0][0];
+    for (int i = threadIdx.x * 4; i < 3 * kBins; i += kNT * 4) *(uint4*)&h[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
-  // wave reduction, then one LDS atomic per wave
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    o |= __shfl_xor(o, s, 64);
-    an &= __shfl_xor(an, s, 64);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    atomicOr(&sh.orv, o);
-    atomicAnd(&sh.andv, an);
-  }
-  __syncthreads();
-  const uint32_t diff = sh.orv ^ sh.andv;
+  uint32_t orv = lane < kWaves ? sh.wor[lane] : 0u, andv = lane < kWaves ? sh.wand[lane] : 0xFFFFFFFFu;
+  wave_or_and(orv, andv);
+  const uint32_t diff = orv ^ andv;
   if (diff == 0u) {  // every valid key equal
-    T = sh.orv;
+    T = orv;
     rem = (uint32_t)k;
     return;
   }
   const int hb = 31 - __builtin_clz(diff);   // highest differing bit
   uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
-  uint32_t prefix = sh.andv & mask, r = (uint32_t)k;
+  uint32_t prefix = andv & mask, r = (uint32_t)k;
   int top = hb + 1;   // bits [0, top) remain
-  while (top > 0) {
+  for (int p = 0; top > 0; ++p) {
     const int width = top > 11 ? 11 : top;
     const int shift = top - width;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = 0;
-    __syncthreads();
+    uint32_t* h = sh.hist[p];
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1u);
+      if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&h[(key[e] >> shift) & dmask], 1u);
     __syncthreads();
-    // suffix sums over bins: thread t owns bins 2047 - 2t and 2046 - 2t (descending)
-    const uint32_t c0 = sh.hist[kBins - 1 - 2 * threadIdx.x], c1 = sh.hist[kBins - 2 - 2 * threadIdx.x];
+    // descending bins: thread t owns bins 2047 - 2t and 2046 - 2t
+    const uint32_t c0 = h[kBins - 1 - 2 * threadIdx.x], c1 = h[kBins - 2 - 2 * threadIdx.x];
+    const uint32_t incl = wave_incl_scan(c0 + c1);
+    if (lane == 63) sh.wsum[wid] = incl;
+    __syncthreads();
     uint32_t tot;
-    const uint32_t above = block_exclusive_scan(c0 + c1, sh.wsum, tot);
+    const uint32_t above = waves_before(sh.wsum, tot) + incl - (c0 + c1);
     if (above < r && r <= above + c0) {
       sh.bin = kBins - 1 - 2 * threadIdx.x;
       sh.rem = r - above;
@@ -138,7 +147,6 @@ __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uin
     mask |= dmask << shift;
     r = sh.rem;
     top = shift;
-    __syncthreads();
   }
   T = prefix;
   rem = r;
@@ -148,7 +156,8 @@ __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uin
 // (wave-major, then e, then lane).
 template <int E, typename Emit>
 __device__ void ordered_select(const uint32_t (&key)[E], uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -160,12 +169,18 @@ __device__ void ordered_select(const uint32_t (&key)[E], uint32_t T, uint32_t re
     sh.weq[wid] = eq;
   }
   __syncthreads();
-  uint32_t eq_base = 0, pos_base = 0;
-  for (int w = 0; w < wid; ++w) {
-    const uint32_t we = sh.weq[w];
-    const uint32_t take = eq_base >= rem ? 0u : (rem - eq_base < we ? rem - eq_base : we);
-    pos_base += sh.wgt[w] + take;
-    eq_base += we;
+  // per wave (lane l < kWaves stands for wave l): keys equal to T before it, how many
+  // of its own it takes, and the rank of its first selected key
+  uint32_t eq_base, pos_base;
+  {
+    const uint32_t ge = lane < kWaves ? sh.wgt[lane] : 0u, we = lane < kWaves ? sh.weq[lane] : 0u;
+    const uint32_t eq_incl = wave_incl_scan(we);
+    const uint32_t eq_before = eq_incl - we;
+    const uint32_t take = eq_before >= rem ? 0u : (rem - eq_before < we ? rem - eq_before : we);
+    const uint32_t pos_incl = wave_incl_scan(ge + take);
+    const int w0 = wid - 1;
+    eq_base = wid == 0 ? 0u : __builtin_amdgcn_readlane(eq_incl, w0);
+    pos_base = wid == 0 ? 0u : __builtin_amdgcn_readlane(pos_incl, w0);
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
