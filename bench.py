@@ -163,8 +163,8 @@ def main():
 
     # warmup; its last steps time every call (one HIP event between calls) to find the
     # dominant call, which the timed region then brackets alone
-    W = max(args.warmup, 1)
-    n_probe = min(W, 10)
+    W = max(args.warmup, 3)
+    n_probe = min(8, W - 2)   # the first warmup steps load code objects; they are not probed
     wev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_probe)]
     for i in range(W):
         ls = launches[i % len(launches)]
@@ -178,7 +178,7 @@ def main():
             for f in ls:
                 f()
     torch.cuda.synchronize()
-    warm_ms = {n: float(np.mean([wev[j][c].elapsed_time(wev[j][c + 1]) for j in range(n_probe)]))
+    warm_ms = {n: float(np.median([wev[j][c].elapsed_time(wev[j][c + 1]) for j in range(n_probe)]))
                for c, n in enumerate(names)}
     dom = max(["indexer", "topk", "attention"], key=lambda n: warm_ms[n])
     di = names.index(dom)
@@ -282,7 +282,7 @@ def main():
                    "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": args.replicas,
                    "value_bytes_per_step": lat_bytes + key_bytes,
                    "launches": "eager, marshalled once; HIP events around the dominant call only",
-                   "kernels_timing": "dominant call: the timed region; the others: the last warmup steps"},
+                   "kernels_timing": "dominant call: mean over the timed region; the others: median of the last warmup steps"},
         "roofline": roofline,
         "kernels": kern,
         "prefill_indexer": prefill,
