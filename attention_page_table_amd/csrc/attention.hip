@@ -658,11 +658,20 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   write_out<16, F>(a, sh, o, r, split, h0, wave, lane, tid);
 }
 
-// Combine the splits of one (row, head): 256 threads x 2 columns, weights in LDS.
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+// Combine the splits of one (row, head): 512 threads, one column each. The partial
+// outputs of the first 16 splits are loaded before the split weights are known, so
+// the two dependent rounds of loads overlap.
+constexpr int kMergeBatch = 16;
+
+__global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
   __shared__ float wgt[64];
   __shared__ float tot[2];
   const int r = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
+  const int d = threadIdx.x;
+  const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + d;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = u < a.nsplit ? po[(int64_t)u * 32 * kLatent] : 0.f;
   const float* pml = a.part_ml + (int64_t)r * a.nsplit * 64;
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
@@ -690,35 +699,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   __syncthreads();
   const float L = tot[0];
-  const int d = threadIdx.x * 2;
-  const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + d;
-  float2 acc = make_float2(0.f, 0.f);
-  int s = 0;
-  for (; s + 8 <= a.nsplit; s += 8) {
-    float2 v[8];
+  float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *(const float2*)(po + (int64_t)(s + u) * 32 * kLatent);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float f = wgt[s + u];
-      if (f != 0.f) {
-        acc.x += v[u].x * f;
-        acc.y += v[u].y * f;
-      }
-    }
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const float f = u < a.nsplit ? wgt[u] : 0.f;
+    if (f != 0.f) acc += v[u] * f;
   }
-  for (; s < a.nsplit; ++s) {
+  for (int s = kMergeBatch; s < a.nsplit; ++s) {
     const float f = wgt[s];
-    if (f != 0.f) {
-      const float2 v = *(const float2*)(po + (int64_t)s * 32 * kLatent);
-      acc.x += v.x * f;
-      acc.y += v.y * f;
-    }
+    if (f != 0.f) acc += po[(int64_t)s * 32 * kLatent] * f;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float2 res = make_float2(acc.x * inv, acc.y * inv);
-  if (L != L) res = make_float2(L, L);
-  *(float2*)(a.out + ((int64_t)r * a.n_heads + h) * kLatent + d) = res;
+  a.out[((int64_t)r * a.n_heads + h) * kLatent + d] = L != L ? L : acc * inv;
   if (a.lse && threadIdx.x == 0)
     a.lse[(int64_t)r * a.n_heads + h] =
         L != L ? L : (L > 0.f ? (tot[1] + log2f(L)) * 0.69314718055994531f : -__builtin_inff());
@@ -805,7 +797,7 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
   }
   tf_status s = launch_status("tf_sparse_mla_attn");
   if (s != TF_OK || p.nsplit == 1) return s;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(512), 0, st, a);
   return launch_status("tf_sparse_mla_attn");
 }
 
