@@ -59,7 +59,7 @@ struct AttnArgs {
 };
 
 template <int HG>
-struct AttnShared {
+struct alignas(16) AttnShared {
   __bf16 kv[kTileTok][kRS];
   float spart[HG == 32 ? 4 : 2][HG][kTileTok + 1];
   __bf16 p_hi[HG][kTileTok + 8];
@@ -306,7 +306,7 @@ __device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const fl
 }
 
 // Final normalization (one split) or the split's partial (O, max, sum).
-template <int HG, typename F, typename SH>
+template <int HG, typename F, typename SH, int NT = F::kNT, int WCOLS = 128>
 __device__ __forceinline__ void write_out(const AttnArgs& a, SH& sh, const typename F::acc_t* o, int r, int split,
                                           int h0, int wave, int lane, int tid) {
   const int col = F::a_row(lane);
@@ -320,9 +320,9 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, SH& sh, const typen
       if (head >= a.n_heads) continue;
       const float l = sh.l_run[m];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float* orow = a.out + ((int64_t)r * a.n_heads + head) * kLatent + wave * 128 + col;
+      float* orow = a.out + ((int64_t)r * a.n_heads + head) * kLatent + wave * WCOLS + col;
 #pragma unroll
-      for (int nt = 0; nt < F::kNT; ++nt) orow[nt * F::kNTW] = bad ? qnan : o[nt][i] * inv;
+      for (int nt = 0; nt < NT; ++nt) orow[nt * F::kNTW] = bad ? qnan : o[nt][i] * inv;
     }
     if (a.lse && tid < HG && h0 + tid < a.n_heads) {
       const float l = sh.l_run[tid];
@@ -334,9 +334,9 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, SH& sh, const typen
 #pragma unroll
     for (int i = 0; i < F::kAccN; ++i) {
       const int m = F::row_of(i, lane);
-      float* orow = po + (int64_t)(h0 + m) * kLatent + wave * 128 + col;
+      float* orow = po + (int64_t)(h0 + m) * kLatent + wave * WCOLS + col;
 #pragma unroll
-      for (int nt = 0; nt < F::kNT; ++nt) orow[nt * F::kNTW] = o[nt][i];
+      for (int nt = 0; nt < NT; ++nt) orow[nt * F::kNTW] = o[nt][i];
     }
     if (tid < HG) {
       float* pm = a.part_ml + (((int64_t)r * a.nsplit + split) * 32 + h0 + tid) * 2;
@@ -465,35 +465,42 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 }
 
 // ---- decode: every row of the workgroup in LDS at once ------------------------------------
-// Few rows (decode): a workgroup owns 16 heads and at most 128 tokens of one row.
-// All of its latent rows go global -> LDS directly (one 1 KiB wave-wide load per
-// token, no registers) and its rope rows eight tokens per load, so every byte the
-// workgroup needs is in flight at once. Then one pass: S for all 128 tokens (wave w
-// takes tokens 32w..32w+31 with four independent MFMA chains), one softmax per head
-// (no running rescale), and O = P V with K = 128. bf16 rows only.
+// Few rows (decode): a workgroup of 8 waves owns 16 heads and at most 128 tokens of
+// one row; wave w owns tokens 16w .. 16w + 15 from the page lookup to S:
+//   * the loads that need nothing go out first: the wave's block ids and a third of
+//     the queries (global -> LDS, so the workgroup reads its 18 KiB of queries once);
+//     then the page ids; then every latent row of the wave goes global -> LDS
+//     directly (one 1 KiB wave-wide load per token, no registers) and its rope rows
+//     into registers, already in MFMA B-fragment order;
+//   * S for the wave's 16 tokens on v_mfma_f32_16x16x32_bf16 (heads as M), kept in
+//     registers; the per-head maxima and sums cross waves through LDS (two barriers);
+//   * O = P V with K = 128: wave w owns columns 64w .. 64w + 63, P as a bf16 hi + lo
+//     pair, V read transposed from the latent tile.
+// bf16 rows only.
 constexpr int kDecTok = 128;
+constexpr int kDecWaves = 8;
 constexpr int kDecRS = kLatent + 16;   // bf16 per LDS latent row (1,056 bytes: conflict-free transposes)
-constexpr int kDecSS = kDecTok + 4;    // fp32 per S row
 constexpr int kDecPS = kDecTok + 8;    // bf16 per P row
 typedef __attribute__((address_space(3))) void lds_void;
 
-struct DecShared {
+struct alignas(16) DecShared {
   __bf16 lat[kDecTok][kDecRS];
-  __bf16 rope[kDecTok][kRope];
-  union {                        // S, then (after every thread has read its S) P as hi + lo
-    float s[16][kDecSS];
-    struct {
+  union {
+    // queries, read by S only: k-step ks (32 dims) of head h, dims 8g .. 8g + 7 at
+    // q[ks][g][h], so one A fragment is 1 KiB of consecutive bytes
+    __bf16 q[18][4][16][8];
+    struct {                     // then P as hi + lo
       __bf16 hi[16][kDecPS];
       __bf16 lo[16][kDecPS];
     } p;
-  } sp;
-  int32_t tt[kDecTok];
-  int64_t tlat[kDecTok];         // byte offset of the token's latent row, -1 when not attended
+  } qp;
+  float wmax[kDecWaves][16], wsum[kDecWaves][16];
   float m_run[16], l_run[16];
+  int32_t wbad[kDecWaves];       // a wave's selected token the table could not name
   int32_t bad;
 };
 
-__global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   typedef Frag<16> F;
   __shared__ DecShared sh;
   const int tid = threadIdx.x;
@@ -509,177 +516,213 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   if (unit >= a.n_units) return;
   const int r = unit % a.n_rows, split = unit / a.n_rows;
   const int h0 = hg * 16;
-  const int b = a.row_stream[r];
-  const int t = a.row_pos[r];
   const int j0 = split * a.slots_per_split;
   const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
-  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
-  const int ntiles = (ntok + kTileTok - 1) / kTileTok;   // <= 4
-  const int nt32 = ntiles * kTileTok;
 
-  if (tid == 0) sh.bad = 0;
-  __syncthreads();
-  if (tid < kDecTok) {
-    const int slot = j0 + tid / kPoolRatio;
-    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
-    const int s = blk * kPoolRatio + (tid & 3);
-    int32_t e = kMasked;
-    int64_t off = -1;
-    if (blk >= 0 && s <= t) {
-      const int page = page_of(a.v, b, s / kPageRows);
-      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
-      if (page >= 0) off = row_base(a, e) + (int64_t)(e & 511) * a.lat_row_bytes;
-      else sh.bad = 1;
-    }
-    sh.tt[tid] = e;
-    sh.tlat[tid] = off;
-  }
-  // query fragments: all 18 k-steps (32 dims each) of this lane's head
-  bf16x8 aq[18];
+  // ---- loads with no dependence ------------------------------------------------------
+  // Every address is made valid by clamping, so the loads carry no branches and stay
+  // in flight together; what a clamped load returns is discarded by the selects below.
+  // Lane i < 16 stands for token 16w + i (block slot j0 + 4w + i/4).
+  const int b = a.row_stream[r];
+  const int t = a.row_pos[r];
+  const int slot = j0 + 4 * wave + ((lane >> 2) & 3);
+  const int blk_raw = a.blocks[(int64_t)r * a.k + (slot < a.k ? slot : a.k - 1)];
   {
-    const int head = h0 + (lane & 15);
-    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + head) * kRow + (lane >> 4) * 8;
+    // query k-steps w, w + 8 and w + 16 (waves 2.. load k-step w again: same bytes)
+    const int hq = h0 + (lane & 15) < a.n_heads ? h0 + (lane & 15) : a.n_heads - 1;   // heads past n_heads are never written
+    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + hq) * kRow + (lane >> 4) * 8;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) aq[ks] = head < a.n_heads ? *(const bf16x8*)(qr + ks * 32) : bf16x8{};
-  }
-  __syncthreads();
-  // ---- every load of the workgroup at once -----------------------------------------
-  // wave w owns tokens w, w + 4, ... (lane i: token w + 4i); rope groups of 8 tokens
-  // w, w + 4, ... (lane l: token 8g + l/8, piece l%8). Offsets are read before any
-  // load is issued, so no wait falls between the loads.
-  const int my_n = (nt32 - wave + 3) / 4;
-  const int64_t my_off = lane < my_n ? sh.tlat[wave + 4 * lane] : -1;
-  const char* rsrc[4];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int g8 = wave + 4 * q4;
-    const int tok = g8 * 8 + (lane >> 3);
-    const int32_t e = tok < nt32 ? sh.tt[tok] : kMasked;
-    rsrc[q4] = e >= 0 ? a.v.pool + row_base(a, e) + a.off_rope + (int64_t)(e & 511) * (kRope * 2) + (lane & 7) * 16
-                      : a.v.pool + (lane & 7) * 16;   // any readable bytes: masked tokens never reach P V
-  }
-  uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)(my_off >> 32);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < my_n) {
-      const uint32_t lo = __builtin_amdgcn_readlane(off_lo, i);
-      const uint32_t hi = __builtin_amdgcn_readlane(off_hi, i);
-      const int64_t off = (int64_t)(((uint64_t)hi << 32) | lo);
-      if (off >= 0)
-        __builtin_amdgcn_global_load_lds((const void*)(a.v.pool + off + lane * 16),
-                                         (lds_void*)&sh.lat[wave + 4 * i][0], 16, 0, 0);
+    for (int u = 0; u < 3; ++u) {
+      const int ks = u < 2 ? wave + 8 * u : (wave < 2 ? wave + 16 : wave);
+      __builtin_amdgcn_global_load_lds((const void*)(qr + ks * 32), (lds_void*)&sh.qp.q[ks][0][0][0], 16, 0, 0);
     }
   }
+  __asm__ volatile("" ::: "memory");
+  const int blk = lane < 16 && slot < j1 ? blk_raw : -1;
+
+  // ---- page of each token; byte offsets of its latent and rope rows -------------------
+  const int s = blk * kPoolRatio + (lane & 3);
+  const bool sel = blk >= 0 && s <= t;
+  const int pi = s / kPageRows;
+  const bool in_tab = sel && pi < a.v.pt_stride && b >= 0 && b < a.v.n_streams;
+  const int64_t pidx = in_tab ? (int64_t)b * a.v.pt_stride + pi : 0;
+  const int pg = a.v.pt ? a.v.pt[pidx] : (int)pidx;
+  const int page = in_tab && pg >= 0 && pg < a.v.n_pages ? pg : -1;
+  const bool valid = page >= 0;
+  const int64_t base = valid ? (int64_t)page * a.v.page_bytes + a.v.cache_off : -1;
+  const int64_t lat_off = valid ? base + (int64_t)(s % kPageRows) * a.lat_row_bytes : -1;
+  const int64_t rope_off = valid ? base + a.off_rope + (int64_t)(s % kPageRows) * (kRope * 2) : 0;
+  const uint64_t vmask = __ballot(valid);
+  const bool wbad = __ballot(sel && !valid) != 0;
+  if (lane == 0) sh.wbad[wave] = wbad;   // read after the barriers below
+
+  // ---- every load of the wave at once ------------------------------------------------
+  const int row0 = 16 * wave;
+  const uint32_t lo_l = (uint32_t)lat_off, hi_l = (uint32_t)((uint64_t)lat_off >> 32);
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int g8 = wave + 4 * q4;
-    if (g8 * 8 < nt32) __builtin_amdgcn_global_load_lds((const void*)rsrc[q4], (lds_void*)&sh.rope[g8 * 8][0], 16, 0, 0);
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = __builtin_amdgcn_readlane(lo_l, i), hi = __builtin_amdgcn_readlane(hi_l, i);
+    const int64_t off = (int64_t)(((uint64_t)hi << 32) | lo);
+    if (off >= 0)
+      __builtin_amdgcn_global_load_lds((const void*)(a.v.pool + off + lane * 16), (lds_void*)&sh.lat[row0 + i][0],
+                                       16, 0, 0);
+  }
+  // rope straight into the B fragments of the two rope k-steps: lane holds dims
+  // 32 ks + 8 (lane / 16) .. + 7 of token lane % 16 (masked tokens read any readable
+  // bytes: their scores never reach the softmax)
+  bf16x8 br[2];
+  {
+    const uint32_t lo_r = (uint32_t)rope_off, hi_r = (uint32_t)((uint64_t)rope_off >> 32);
+    const uint64_t ro = ((uint64_t)(uint32_t)__shfl((int)hi_r, lane & 15, 64) << 32) |
+                        (uint32_t)__shfl((int)lo_r, lane & 15, 64);
+    const char* rsrc = a.v.pool + ro + (lane >> 4) * 16;
+    br[0] = *(const bf16x8*)rsrc;
+    br[1] = *(const bf16x8*)(rsrc + 64);
   }
   // rows not attended are zero (P V multiplies them by 0)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < my_n && (int32_t)__builtin_amdgcn_readlane(off_hi, i) < 0)
-      *(uint4*)&sh.lat[wave + 4 * i][lane * 8] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
+  for (int i = 0; i < 16; ++i)
+    if (!((vmask >> i) & 1)) *(uint4*)&sh.lat[row0 + i][lane * 8] = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's rows and query k-steps have landed
+  __syncthreads();                      // every wave's query k-steps
 
-  // ---- S for tokens 32w .. 32w + 31: two 16-token N tiles x two k halves ------------
-  if (wave < ntiles) {
-    f32x4 acc[2][2] = {};
-    const int tok0 = wave * kTileTok + (lane & 15);
+  // ---- S for the wave's 16 tokens: lane holds heads 4(lane/16) .. + 3 of token lane % 16 ----
+  float z[4];
+  {
+    f32x4 acc[2] = {};
+    const int tok = row0 + (lane & 15);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-#pragma unroll
-      for (int n2 = 0; n2 < 2; ++n2) {
-        const int tok = tok0 + 16 * n2;
-        const int d = ks * 32 + (lane >> 4) * 8;
-        const bf16x8 bk = ks < 16 ? *(const bf16x8*)&sh.lat[tok][d] : *(const bf16x8*)&sh.rope[tok][d - kLatent];
-        acc[n2][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], bk, acc[n2][ks & 1], 0, 0, 0);
-      }
+      const bf16x8 aq = *(const bf16x8*)&sh.qp.q[ks][lane >> 4][lane & 15][0];
+      const bf16x8 bk = ks < 16 ? *(const bf16x8*)&sh.lat[tok][ks * 32 + (lane >> 4) * 8] : br[ks - 16];
+      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, acc[ks & 1], 0, 0, 0);
     }
+    const bool att = (vmask >> (lane & 15)) & 1;
 #pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sh.sp.s[4 * (lane >> 4) + i][wave * kTileTok + 16 * n2 + (lane & 15)] =
-            (acc[n2][0][i] + acc[n2][1][i]) * a.scale_log2;
+    for (int i = 0; i < 4; ++i) {
+      z[i] = att ? (acc[0][i] + acc[1][i]) * a.scale_log2 : -__builtin_inff();
+      const float m = group_max<16>(z[i]);
+      if ((lane & 15) == 0) sh.wmax[wave][4 * (lane >> 4) + i] = m;
+    }
   }
-  __syncthreads();
-  // ---- softmax: 16 threads per head, 8 tokens each ----------------------------------
+  __syncthreads();   // every wave's maxima; every wave is past its reads of the queries
   {
-    const int h = tid >> 4, p = tid & 15;
-    float z[8];
-    float mx = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = p * 8 + e;
-      const float v = tok < nt32 && sh.tt[tok] >= 0 ? sh.sp.s[h][tok] : -__builtin_inff();
-      z[e] = v;
-      mx = __builtin_fmaxf(mx, v);
-    }
-    mx = group_max<16>(mx);
-    float sum = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * (lane >> 4) + i;
+      float m = sh.wmax[0][h];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      z[e] = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - mx);
-      sum += z[e];
-    }
-    sum = group_sum<16>(sum);
-    __syncthreads();   // S is read by every thread before P overwrites it
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 hi = bf16_rne(z[e]);
-      sh.sp.p.hi[h][p * 8 + e] = hi;
-      sh.sp.p.lo[h][p * 8 + e] = bf16_rne(z[e] - bf16_to_f(hi));
-    }
-    if (p == 0) {
-      sh.m_run[h] = mx;
-      sh.l_run[h] = sum;
+      for (int w = 1; w < kDecWaves; ++w) m = __builtin_fmaxf(m, sh.wmax[w][h]);
+      const float p = z[i] == -__builtin_inff() ? 0.f : exp2f(z[i] - m);
+      const float ps = group_sum<16>(p);
+      if ((lane & 15) == 0) sh.wsum[wave][h] = ps;
+      if (wave == 0 && (lane & 15) == 0) sh.m_run[h] = m;
+      const __bf16 hi = bf16_rne(p);
+      sh.qp.p.hi[h][row0 + (lane & 15)] = hi;
+      sh.qp.p.lo[h][row0 + (lane & 15)] = bf16_rne(p - bf16_to_f(hi));
     }
   }
   __syncthreads();
-  // ---- O = P V: wave w owns columns 128w .. 128w + 127 (8 tiles of 16) ---------------
-  F::acc_t o[F::kNT];
+  if (tid < 16) {
+    float l = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < F::kNT; ++nt) o[nt] = F::acc_t{};
+    for (int w = 0; w < kDecWaves; ++w) l += sh.wsum[w][tid];
+    sh.l_run[tid] = l;
+  }
+  if (tid == 16) {
+    int32_t bad = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) bad |= sh.wbad[w];
+    sh.bad = bad;
+  }
+  // ---- O = P V: wave w owns columns 64w .. 64w + 63 (4 tiles of 16) ---------------------
+  constexpr int kNTd = 4;
+  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
+  const int nks = (ntok + 31) / 32;   // k-steps of 32 tokens holding any selected token
+  F::acc_t o[kNTd];
+#pragma unroll
+  for (int nt = 0; nt < kNTd; ++nt) o[nt] = F::acc_t{};
   {
     const int arow = lane & 15, grp = lane >> 4, j = lane & 15;
-    for (int ks = 0; ks < ntiles; ++ks) {
-      const bf16x8 ph = *(const bf16x8*)&sh.sp.p.hi[arow][ks * 32 + grp * 8];
-      const bf16x8 pl = *(const bf16x8*)&sh.sp.p.lo[arow][ks * 32 + grp * 8];
+    for (int ks = 0; ks < nks; ++ks) {
+      const bf16x8 ph = *(const bf16x8*)&sh.qp.p.hi[arow][ks * 32 + grp * 8];
+      const bf16x8 pl = *(const bf16x8*)&sh.qp.p.lo[arow][ks * 32 + grp * 8];
 #pragma unroll
-      for (int nt = 0; nt < F::kNT; ++nt) {
-        const bf16x8 vb = bfrag_tr(&sh.lat[0][0], kDecRS, ks * 32 + grp * 8, wave * 128 + nt * 16, j);
+      for (int nt = 0; nt < kNTd; ++nt) {
+        const bf16x8 vb = bfrag_tr(&sh.lat[0][0], kDecRS, ks * 32 + grp * 8, wave * 64 + nt * 16, j);
         o[nt] = F::mfma(ph, vb, o[nt]);
         o[nt] = F::mfma(pl, vb, o[nt]);
       }
     }
   }
-  write_out<16, F>(a, sh, o, r, split, h0, wave, lane, tid);
+  __syncthreads();   // l_run, bad
+  // ---- output: the wave's 16 x 64 block of O goes through LDS (the latent-tile columns
+  // only this wave read in P V) so that each lane stores whole float4 runs of a row ----
+  {
+    float* ob = (float*)&sh.lat[0][wave * 64];   // 32 floats per latent-tile row
+    constexpr int kOS = kDecRS / 2;
+#pragma unroll
+    for (int nt = 0; nt < kNTd; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = (4 * (lane >> 4) + i) * 64 + nt * 16 + (lane & 15);   // head * 64 + column
+        ob[(f >> 5) * kOS + (f & 31)] = o[nt][i];
+      }
+    const bool bad = sh.bad != 0;
+    const int c4 = 4 * (lane & 15);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int h = 4 * pp + (lane >> 4);
+      const int f = h * 64 + c4;
+      float4 v = *(const float4*)&ob[(f >> 5) * kOS + (f & 31)];
+      if (a.nsplit == 1) {
+        if (h0 + h < a.n_heads) {
+          const float l = sh.l_run[h];
+          const float inv = l > 0.f ? 1.f / l : 0.f;
+          v = bad ? make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""))
+                  : make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+          *(float4*)(a.out + ((int64_t)r * a.n_heads + h0 + h) * kLatent + wave * 64 + c4) = v;
+        }
+      } else {
+        *(float4*)(a.part_o + (((int64_t)r * a.nsplit + split) * 32 + h0 + h) * kLatent + wave * 64 + c4) = v;
+      }
+    }
+    if (wave == 0 && lane < 16) {
+      const float l = sh.l_run[lane], m = sh.m_run[lane];
+      if (a.nsplit == 1) {
+        if (a.lse && h0 + lane < a.n_heads)
+          a.lse[(int64_t)r * a.n_heads + h0 + lane] =
+              bad ? __builtin_nanf("") : (l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff());
+      } else {
+        float* pm = a.part_ml + (((int64_t)r * a.nsplit + split) * 32 + h0 + lane) * 2;
+        pm[0] = m;
+        pm[1] = bad ? __builtin_nanf("") : l;
+      }
+    }
+  }
 }
 
-// Combine the splits of one (row, head): 512 threads, one column each. The partial
+// Combine the splits of one (row, head): 128 threads, four columns each. The partial
 // outputs of the first 16 splits are loaded before the split weights are known, so
 // the two dependent rounds of loads overlap.
 constexpr int kMergeBatch = 16;
 
-__global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
   __shared__ float wgt[64];
   __shared__ float tot[2];
   const int r = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
-  const int d = threadIdx.x;
-  const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + d;
-  float v[kMergeBatch];
+  const int c4 = 4 * threadIdx.x;
+  const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + c4;
+  float4 v[kMergeBatch];
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) v[u] = u < a.nsplit ? po[(int64_t)u * 32 * kLatent] : 0.f;
+  for (int u = 0; u < kMergeBatch; ++u)   // clamped split index: a split past nsplit gets weight 0
+    v[u] = *(const float4*)(po + (int64_t)(u < a.nsplit ? u : a.nsplit - 1) * 32 * kLatent);
   const float* pml = a.part_ml + (int64_t)r * a.nsplit * 64;
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
-    float m = -__builtin_inff(), l = 0.f;
-    if (s < a.nsplit) {
-      m = pml[(s * 32 + h) * 2];
-      l = pml[(s * 32 + h) * 2 + 1];
-    }
+    const float2 ml = *(const float2*)&pml[((s < a.nsplit ? s : a.nsplit - 1) * 32 + h) * 2];
+    const float m = s < a.nsplit ? ml.x : -__builtin_inff();
+    const float l = s < a.nsplit ? ml.y : 0.f;
     bool nan = (m != m) || (l != l);
     float M = l > 0.f ? m : -__builtin_inff();
 #pragma unroll
@@ -699,18 +742,28 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
   }
   __syncthreads();
   const float L = tot[0];
-  float acc = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u) {
-    const float f = u < a.nsplit ? wgt[u] : 0.f;
-    if (f != 0.f) acc += v[u] * f;
+    const float f = u < a.nsplit ? wgt[u] : 0.f;   // a split without an attended token has weight 0
+    acc.x += f != 0.f ? v[u].x * f : 0.f;
+    acc.y += f != 0.f ? v[u].y * f : 0.f;
+    acc.z += f != 0.f ? v[u].z * f : 0.f;
+    acc.w += f != 0.f ? v[u].w * f : 0.f;
   }
   for (int s = kMergeBatch; s < a.nsplit; ++s) {
     const float f = wgt[s];
-    if (f != 0.f) acc += po[(int64_t)s * 32 * kLatent] * f;
+    if (f != 0.f) {
+      const float4 x = *(const float4*)(po + (int64_t)s * 32 * kLatent);
+      acc.x += x.x * f;
+      acc.y += x.y * f;
+      acc.z += x.z * f;
+      acc.w += x.w * f;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  a.out[((int64_t)r * a.n_heads + h) * kLatent + d] = L != L ? L : acc * inv;
+  *(float4*)(a.out + ((int64_t)r * a.n_heads + h) * kLatent + c4) =
+      L != L ? make_float4(L, L, L, L) : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (a.lse && threadIdx.x == 0)
     a.lse[(int64_t)r * a.n_heads + h] =
         L != L ? L : (L > 0.f ? (tot[1] + log2f(L)) * 0.69314718055994531f : -__builtin_inff());
@@ -785,9 +838,9 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
   a.out = out;
   a.lse = lse;
   a.part_o = p.nsplit > 1 ? (float*)ws : nullptr;
-  a.part_ml = p.nsplit > 1 ? (float*)ws + (size_t)n_rows * p.nsplit * 32 * kLatent : nullptr;
+  a.part_ml = p.nsplit > 1 ? a.part_o + (size_t)n_rows * p.nsplit * 32 * kLatent : nullptr;
   if (p.decode) {
-    hipLaunchKernelGGL(attn_decode_kernel, dim3(p.grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_decode_kernel, dim3(p.grid), dim3(512), 0, st, a);
   } else if (p.hg == 16) {
     if (fp8) hipLaunchKernelGGL((attn_kernel<16, true>), dim3(p.grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_kernel<16, false>), dim3(p.grid), dim3(256), 0, st, a);
@@ -797,7 +850,7 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
   }
   tf_status s = launch_status("tf_sparse_mla_attn");
   if (s != TF_OK || p.nsplit == 1) return s;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(512), 0, st, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(128), 0, st, a);
   return launch_status("tf_sparse_mla_attn");
 }
 
