@@ -61,7 +61,8 @@ __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
 // A-rows with bit 2 clear carry the row's heads (head 4 * (m / 8) + m % 4), the others are
 // zero; lanes 0..31 then hold every head of key n = lane in accumulators 0..H-1.
 template <int H, int D>
-__device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke, int lane) {
+__device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke, int lane, bool spec_page = false,
+                              int spec_page_all = -1) {
   constexpr int KS = D / 16;
   const int g = lane >> 5, n = lane & 31;
   const int b = a.row_stream[row];
@@ -83,7 +84,15 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
   const int64_t kend = ke < nc ? ke : nc;   // keys that need scores
   // page ids of the range, one per lane (lane i: page index kb/128 + i)
   const int p0 = (int)(kb / kKeysPerPage);
-  const int my_page = page_of(a.v, b, p0 + lane);
+  int my_page;
+  if (spec_page) {
+    // a one-page range of a table of at most 64 streams: lane s has already read
+    // stream s's entry, so the page id does not wait for the row's stream id
+    const int pb = b >= 0 && b < a.v.n_streams ? __builtin_amdgcn_readlane(spec_page_all, b) : -1;
+    my_page = lane == 0 ? pb : -1;
+  } else {
+    my_page = page_of(a.v, b, p0 + lane);
+  }
   auto page_at = [&](int64_t kt) { return __builtin_amdgcn_readlane(my_page, (int)(kt / kKeysPerPage) - p0); };
   auto load = [&](int64_t kt, bf16x8 (&bf)[KS]) {
     const int pg = page_at(kt);
@@ -136,8 +145,19 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
   if (row >= a.n_rows) return;
   const int64_t kb = (int64_t)kg * a.keys_per_wg;
   const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  // one-page ranges over a table of at most 64 streams: read every stream's entry for
+  // the page now, beside the row's own stream id
+  const bool spec = a.keys_per_wg == kKeysPerPage && a.v.n_streams <= 64;
+  int spec_all = -1;
+  if (spec) {
+    const int pi = (int)(kb / kKeysPerPage);
+    if (lane < a.v.n_streams && pi < a.v.pt_stride) {
+      const int pg = a.v.pt ? a.v.pt[(int64_t)lane * a.v.pt_stride + pi] : lane * a.v.pt_stride + pi;
+      spec_all = pg >= 0 && pg < a.v.n_pages ? pg : -1;
+    }
+  }
   if (kg == 0 && a.n_valid && lane == 0) a.n_valid[row] = nc_of(a, row);
-  index_one_row<H, D>(a, row, kb, ke, lane);
+  index_one_row<H, D>(a, row, kb, ke, lane, spec, spec_all);
 }
 
 // ---- tile path -----------------------------------------------------------------------------
@@ -377,9 +397,10 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
     hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT>), dim3((unsigned)kgroups, (unsigned)rgroups), dim3(256), 0,
                        st, a);
   } else {
-    // each wave one row; about 1,024 waves in all; a wave's range spans at most 64 pages
+    // each wave one row; about 2,048 waves in all (eight per CU keep more key loads in
+    // flight than four); a wave's range spans at most 64 pages
     const int n_rg = (n_rows + 3) / 4;
-    int64_t kpw = (a.ld * n_rows + 1023) / 1024;
+    int64_t kpw = (a.ld * n_rows + 2047) / 2048;
     kpw = (kpw + 127) / 128 * 128;
     if (kpw < 128) kpw = 128;
     if (kpw > 64 * 128) kpw = 64 * 128;

@@ -5,16 +5,18 @@
 // topk(union) == topk(union of per-block topk).
 //
 // Design: a workgroup of 1,024 threads owns a segment of up to 32,768 keys held in
-// registers; wave w owns the contiguous index range [w*64E, (w+1)*64E) and its lane l
-// holds indices w*64E + 64e + l (coalesced loads). Logits become order-preserving
-// 32-bit keys. The bits above the highest bit in which the segment's keys differ
-// (from OR/AND reductions) are common; a most-significant-digit radix select over
-// the rest, in passes of at most 11 bits with 2,048-bin LDS histograms, finds the
-// k-th largest key T and how many keys equal to T belong to the top k. An ordered
-// compaction with wave ballots then writes the selected indices ascending, taking
-// keys equal to T lowest index first. No sort is needed because the output order is
-// by index. Long rows: stage 1 selects per key block, stage 2 merges the blocks'
-// candidates (kept in index order).
+// registers; thread t holds the contiguous keys t*E .. t*E + E - 1 (16-byte loads).
+// Logits become order-preserving 32-bit keys. The bits above the highest bit in which
+// the segment's keys differ (from OR/AND reductions) are common; a most-significant-
+// digit radix select over the rest, in passes of at most 11 bits with 2,048-bin LDS
+// histograms, finds the k-th largest key T and how many keys equal to T belong to the
+// top k. Every thread then counts its keys above T and equal to T; one block-wide
+// prefix of the two counts gives each thread where its selected keys go and how many
+// of its keys equal to T it takes, so the indices come out ascending, ties to the
+// lower index, with no sort. Segments of 16 or 32 keys per thread first cut the keys
+// down to a little more than k with a threshold taken from per-group maxima (each
+// radix pass costs an LDS atomic per key and thread). Long rows: stage 1 selects per
+// key block, stage 2 merges the blocks' candidates (kept in index order).
 #include "common.h"
 
 namespace tf {
@@ -45,10 +47,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // OR and AND of a value over the wave: within each row of 16 lanes by DPP, then the
 // four rows through readlane (the results are wave-uniform).
 __device__ __forceinline__ void wave_or_and(uint32_t& o, uint32_t& a) {
@@ -66,9 +64,10 @@ __device__ __forceinline__ void wave_or_and(uint32_t& o, uint32_t& a) {
       __builtin_amdgcn_readlane(a, 48);
 }
 
-struct SelShared {
+struct alignas(16) SelShared {
   uint32_t hist[3][kBins];   // one histogram per radix pass, all cleared up front
-  uint32_t wor[kWaves], wand[kWaves], wsum[kWaves], wgt[kWaves], weq[kWaves];
+  uint32_t wor[kWaves], wand[kWaves], wsum[kWaves];
+  uint32_t scan[2][2][kWaves];   // two buffers of per-wave totals of two counts
   uint32_t bin, rem;
 };
 
@@ -85,8 +84,11 @@ __device__ __forceinline__ uint32_t waves_before(const uint32_t* v, uint32_t& to
 // T = the k-th largest of the n > k valid keys (invalid slots hold 0, below every
 // valid key), rem = how many keys equal to T belong to the top k. Three barriers per
 // radix pass: after the histogram, after the wave totals, after the selected bin.
+// With first_pass_only, T is instead the lowest key of the first pass's bin that holds
+// the k-th largest (at least k keys are >= T) and rem is not set.
 template <int E>
-__device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uint32_t& T, uint32_t& rem) {
+__device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uint32_t& T, uint32_t& rem,
+                             bool first_pass_only = false) {
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // common leading bits of the valid keys; clear the pass histograms
@@ -147,51 +149,166 @@ __device__ void radix_select(const uint32_t (&key)[E], int k, SelShared& sh, uin
     mask |= dmask << shift;
     r = sh.rem;
     top = shift;
+    if (first_pass_only) break;
   }
   T = prefix;
   rem = r;
 }
 
-// Ordered compaction: emit(pos, e) for every selected key, in index order
-// (wave-major, then e, then lane).
-template <int E, typename Emit>
-__device__ void ordered_select(const uint32_t (&key)[E], uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+// Exclusive block-wide prefix (in thread order) of two per-thread counts, and their
+// totals. w is one of the two scan buffers; a caller alternates them, or leaves a
+// barrier between two uses of one buffer.
+__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t (&w)[2][kWaves], uint32_t& a_before,
+                                            uint32_t& b_before, uint32_t& a_tot, uint32_t& b_tot) {
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ai = wave_incl_scan(a), bi = wave_incl_scan(b);
+  if (lane == 63) {
+    w[0][wid] = ai;
+    w[1][wid] = bi;
+  }
+  __syncthreads();
+  const uint32_t aw = waves_before(w[0], a_tot), bw = waves_before(w[1], b_tot);
+  a_before = aw + ai - a;
+  b_before = bw + bi - b;
+}
+
+// emit(pos, e) for the keys above T and the first rem keys equal to T, pos ascending
+// with the index (thread t holds the contiguous keys t*E + e).
+template <int E, typename Emit>
+__device__ __forceinline__ void ordered_emit(const uint32_t (&key)[E], uint32_t T, uint32_t rem,
+                                             uint32_t (&w)[2][kWaves], Emit emit) {
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    gt += __builtin_popcountll(__ballot(key[e] > T));
-    eq += __builtin_popcountll(__ballot(key[e] == T));
+    gt += key[e] > T ? 1u : 0u;
+    eq += key[e] == T ? 1u : 0u;
   }
-  if (lane == 0) {
-    sh.wgt[wid] = gt;
-    sh.weq[wid] = eq;
-  }
-  __syncthreads();
-  // per wave (lane l < kWaves stands for wave l): keys equal to T before it, how many
-  // of its own it takes, and the rank of its first selected key
-  uint32_t eq_base, pos_base;
-  {
-    const uint32_t ge = lane < kWaves ? sh.wgt[lane] : 0u, we = lane < kWaves ? sh.weq[lane] : 0u;
-    const uint32_t eq_incl = wave_incl_scan(we);
-    const uint32_t eq_before = eq_incl - we;
-    const uint32_t take = eq_before >= rem ? 0u : (rem - eq_before < we ? rem - eq_before : we);
-    const uint32_t pos_incl = wave_incl_scan(ge + take);
-    const int w0 = wid - 1;
-    eq_base = wid == 0 ? 0u : __builtin_amdgcn_readlane(eq_incl, w0);
-    pos_base = wid == 0 ? 0u : __builtin_amdgcn_readlane(pos_incl, w0);
-  }
+  uint32_t gt_b, eq_b, gt_t, eq_t;
+  block_scan2(gt, eq, w, gt_b, eq_b, gt_t, eq_t);
+  uint32_t pos = gt_b + (eq_b < rem ? eq_b : rem);
+  uint32_t eq_i = eq_b;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool is_eq = key[e] == T;
-    const uint64_t em = __ballot(is_eq);
-    const bool take = key[e] > T || (is_eq && eq_base + lanes_below(em) < rem);
-    const uint64_t tm = __ballot(take);
-    if (take) emit(pos_base + lanes_below(tm), e);
-    pos_base += __builtin_popcountll(tm);
-    eq_base += __builtin_popcountll(em);
+    if (key[e] > T || (is_eq && eq_i < rem)) emit(pos++, e);
+    eq_i += is_eq ? 1u : 0u;
   }
+}
+
+// Thread t's keys t*E .. t*E + E - 1 of a segment of n (invalid slots: 0). vec: the
+// segment is 16-byte aligned and every group of four that starts before n lies in the
+// row, so groups load as one 16-byte access.
+template <int E>
+__device__ __forceinline__ void load_keys(const float* seg, int n, bool vec, uint32_t (&key)[E]) {
+  const int base = threadIdx.x * E;
+  if (vec) {
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const int i = base + 4 * j;
+      const float4 v = i < n ? *(const float4*)(seg + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      key[4 * j + 0] = i + 0 < n ? order_key(v.x) : 0u;
+      key[4 * j + 1] = i + 1 < n ? order_key(v.y) : 0u;
+      key[4 * j + 2] = i + 2 < n ? order_key(v.z) : 0u;
+      key[4 * j + 3] = i + 3 < n ? order_key(v.w) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(seg[base + e]) : 0u;
+  }
+}
+
+// ---- long segments: a sampled threshold first ---------------------------------------------
+// Each thread splits its keys into S groups (S * 1,024 > k) and offers each group's
+// maximum as a sample. One radix pass over the samples gives T0, the lowest key of the
+// pass's bin that holds the k-th largest sample: at least k samples, which are distinct
+// keys, are >= T0, so the top k lies among the keys >= T0 (ties with the k-th value
+// included). Those candidates, usually a little over k, go in index order into LDS,
+// where the exact selection runs on them, four per thread. With too few samples or too
+// many candidates the caller selects on the whole segment instead.
+constexpr int kCandCap = 4 * kNT;
+
+struct alignas(16) CandShared {
+  uint32_t key[kCandCap];
+  int32_t idx[kCandCap];
+};
+
+// emit(pos, key, idx) for the k selected keys, pos ascending with the index; idx_of(e)
+// names thread key e. False when the caller must select on the whole segment.
+template <int E, int S, typename IdxOf, typename Emit>
+__device__ bool select_sampled(const uint32_t (&key)[E], int k, SelShared& sh, CandShared& cs, IdxOf idx_of,
+                               Emit emit) {
+  static_assert(E % S == 0, "S groups of keys");
+  constexpr int G = E / S;
+  uint32_t smp[S];
+  uint32_t nsmp = 0;
+#pragma unroll
+  for (int c = 0; c < S; ++c) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = c * G; e < (c + 1) * G; ++e) m = key[e] > m ? key[e] : m;
+    smp[c] = m;
+    nsmp += m != 0u ? 1u : 0u;
+  }
+  uint32_t x0, x1, ns, x3;
+  block_scan2(nsmp, 0u, sh.scan[0], x0, x1, ns, x3);
+  if (ns <= (uint32_t)k) return false;
+  uint32_t T0, unused;
+  radix_select<S>(smp, k, sh, T0, unused, true);
+  if (T0 == 0u) T0 = 1u;   // every valid key (invalid slots hold 0)
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += key[e] >= T0 ? 1u : 0u;
+  uint32_t c_b, y1, C, y3;
+  block_scan2(c, 0u, sh.scan[1], c_b, y1, C, y3);
+  if (C > (uint32_t)kCandCap) return false;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (key[e] >= T0) {
+      cs.key[c_b] = key[e];
+      cs.idx[c_b] = idx_of(e);
+      ++c_b;
+    }
+  __syncthreads();
+  if (C == (uint32_t)k) {
+    for (int i = threadIdx.x; i < k; i += kNT) emit((uint32_t)i, cs.key[i], cs.idx[i]);
+    return true;
+  }
+  uint32_t ck[4];
+  int32_t ci[4];
+  {
+    const uint4 kv = *(const uint4*)&cs.key[4 * threadIdx.x];
+    const int4 iv = *(const int4*)&cs.idx[4 * threadIdx.x];
+    const uint32_t kk[4] = {kv.x, kv.y, kv.z, kv.w};
+    const int32_t ii[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = 4 * (int)threadIdx.x + e < (int)C;
+      ck[e] = in ? kk[e] : 0u;
+      ci[e] = in ? ii[e] : -1;
+    }
+  }
+  uint32_t T, rem;
+  radix_select<4>(ck, k, sh, T, rem);
+  ordered_emit<4>(ck, T, rem, sh.scan[0], [&](uint32_t pos, int e) { emit(pos, ck[e], ci[e]); });
+  return true;
+}
+
+// The k largest of a segment's keys (n_valid > k of them), in index order.
+template <int E, typename IdxOf, typename Emit>
+__device__ void select_topk(const uint32_t (&key)[E], int k, SelShared& sh, CandShared& cs, IdxOf idx_of,
+                            Emit emit) {
+  if constexpr (E >= 16) {
+    bool done;
+    if (k < kNT) done = select_sampled<E, 1>(key, k, sh, cs, idx_of, emit);
+    else if (k < 2 * kNT) done = select_sampled<E, 2>(key, k, sh, cs, idx_of, emit);
+    else done = select_sampled<E, 4>(key, k, sh, cs, idx_of, emit);
+    if (done) return;
+    __syncthreads();
+  }
+  uint32_t T, rem;
+  radix_select<E>(key, k, sh, T, rem);
+  ordered_emit<E>(key, T, rem, sh.scan[0], [&](uint32_t pos, int e) { emit(pos, key[e], idx_of(e)); });
 }
 
 struct TopkArgs {
@@ -201,10 +318,12 @@ struct TopkArgs {
   const int32_t* n_valid;
   int32_t k;
   int32_t* blocks;
+  bool vec;           // 16-byte loads of logits rows
   int32_t blk;        // key block length (blocked mode)
   int32_t nblk;       // key blocks per row (blocked mode)
-  uint32_t* ws_key;   // [n_rows][nblk][k]
-  int32_t* ws_idx;    // [n_rows][nblk][k]
+  int32_t kp;         // candidates per block in the workspace: k rounded up to a multiple of 4
+  uint32_t* ws_key;   // [n_rows][nblk][kp]
+  int32_t* ws_idx;    // [n_rows][nblk][kp]
 };
 
 __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
@@ -214,25 +333,11 @@ __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
   return nv;
 }
 
-// index of this thread's e-th key within the segment
-template <int E>
-__device__ __forceinline__ int seg_index(int e) {
-  return (threadIdx.x >> 6) * 64 * E + e * 64 + (threadIdx.x & 63);
-}
-
-template <int E>
-__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&key)[E]) {
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = seg_index<E>(e);
-    key[e] = i < n ? order_key(row[i]) : 0u;
-  }
-}
-
 // One workgroup per row.
 template <int E>
 __global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
   __shared__ SelShared sh;
+  __shared__ CandShared cs;
   const int r = blockIdx.x;
   const int n = row_valid(a, r);
   int32_t* out = a.blocks + (int64_t)r * a.k;
@@ -241,18 +346,18 @@ __global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
     return;
   }
   uint32_t key[E];
-  load_keys<E>(a.logits + (int64_t)r * a.ld, n, key);
-  uint32_t T, rem;
-  radix_select<E>(key, a.k, sh, T, rem);
-  ordered_select<E>(key, T, rem, sh, [&](uint32_t pos, int e) {
-    if (pos < (uint32_t)a.k) out[pos] = seg_index<E>(e);
-  });
+  load_keys<E>(a.logits + (int64_t)r * a.ld, n, a.vec, key);
+  const int base = threadIdx.x * E;
+  select_topk<E>(key, a.k, sh, cs, [&](int e) { return base + e; },
+                 [&](uint32_t pos, uint32_t, int32_t i) { out[pos] = i; });
 }
 
-// Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row.
+// Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row, in
+// index order, padded with key 0 to kp.
 template <int E>
 __global__ __launch_bounds__(kNT) void topk_stage1_kernel(TopkArgs a) {
   __shared__ SelShared sh;
+  __shared__ CandShared cs;
   const int r = blockIdx.y;
   const int bb = blockIdx.x;
   const int nv = row_valid(a, r);
@@ -261,33 +366,35 @@ __global__ __launch_bounds__(kNT) void topk_stage1_kernel(TopkArgs a) {
   int n = nv - i0;
   if (n > a.blk) n = a.blk;
   if (n < 0) n = 0;
-  uint32_t* ck = a.ws_key + ((int64_t)r * a.nblk + bb) * a.k;
-  int32_t* ci = a.ws_idx + ((int64_t)r * a.nblk + bb) * a.k;
+  uint32_t* ck = a.ws_key + ((int64_t)r * a.nblk + bb) * a.kp;
+  int32_t* ci = a.ws_idx + ((int64_t)r * a.nblk + bb) * a.kp;
   const float* row = a.logits + (int64_t)r * a.ld + i0;
   if (n <= a.k) {
-    for (int i = threadIdx.x; i < a.k; i += kNT) {
+    for (int i = threadIdx.x; i < a.kp; i += kNT) {
       ck[i] = i < n ? order_key(row[i]) : 0u;
       ci[i] = i < n ? i0 + i : -1;
     }
     return;
   }
   uint32_t key[E];
-  load_keys<E>(row, n, key);
-  uint32_t T, rem;
-  radix_select<E>(key, a.k, sh, T, rem);
-  ordered_select<E>(key, T, rem, sh, [&](uint32_t pos, int e) {
-    if (pos < (uint32_t)a.k) {
-      ck[pos] = key[e];
-      ci[pos] = i0 + seg_index<E>(e);
-    }
+  load_keys<E>(row, n, a.vec, key);
+  const int base = i0 + threadIdx.x * E;
+  for (int i = a.k + threadIdx.x; i < a.kp; i += kNT) {   // padding past k
+    ck[i] = 0u;
+    ci[i] = -1;
+  }
+  select_topk<E>(key, a.k, sh, cs, [&](int e) { return base + e; }, [&](uint32_t pos, uint32_t kv, int32_t i) {
+    ck[pos] = kv;
+    ci[pos] = i;
   });
 }
 
-// Blocked mode, stage 2: merge the candidates of all key blocks of one row (they
-// are in ascending index order, padding last in each block with key 0).
+// Blocked mode, stage 2: merge the candidates of all key blocks of one row (they are in
+// ascending index order, padding last in each block with key 0).
 template <int E>
 __global__ __launch_bounds__(kNT) void topk_stage2_kernel(TopkArgs a) {
   __shared__ SelShared sh;
+  __shared__ CandShared cs;
   const int r = blockIdx.x;
   const int nv = row_valid(a, r);
   int32_t* out = a.blocks + (int64_t)r * a.k;
@@ -296,33 +403,43 @@ __global__ __launch_bounds__(kNT) void topk_stage2_kernel(TopkArgs a) {
     return;
   }
   const int nb_used = (nv + a.blk - 1) / a.blk;
-  const int n = nb_used * a.k;
-  const uint32_t* ck = a.ws_key + (int64_t)r * a.nblk * a.k;
-  const int32_t* ci = a.ws_idx + (int64_t)r * a.nblk * a.k;
+  const int n = nb_used * a.kp;
+  const uint32_t* ck = a.ws_key + (int64_t)r * a.nblk * a.kp;
+  const int32_t* ci = a.ws_idx + (int64_t)r * a.nblk * a.kp;
   uint32_t key[E];
   int32_t idx[E];
+  const int base = threadIdx.x * E;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = seg_index<E>(e);
-    key[e] = i < n ? ck[i] : 0u;
-    idx[e] = i < n ? ci[i] : -1;
+  for (int j = 0; j < E / 4; ++j) {   // kp is a multiple of 4: whole groups of four
+    const int i = base + 4 * j;
+    const uint4 kv = i < n ? *(const uint4*)(ck + i) : make_uint4(0u, 0u, 0u, 0u);
+    const int4 iv = i < n ? *(const int4*)(ci + i) : make_int4(-1, -1, -1, -1);
+    key[4 * j + 0] = kv.x;
+    key[4 * j + 1] = kv.y;
+    key[4 * j + 2] = kv.z;
+    key[4 * j + 3] = kv.w;
+    idx[4 * j + 0] = iv.x;
+    idx[4 * j + 1] = iv.y;
+    idx[4 * j + 2] = iv.z;
+    idx[4 * j + 3] = iv.w;
   }
-  uint32_t T, rem;
-  radix_select<E>(key, a.k, sh, T, rem);
-  ordered_select<E>(key, T, rem, sh, [&](uint32_t pos, int e) {
-    if (pos < (uint32_t)a.k) out[pos] = idx[e];
-  });
+  select_topk<E>(key, a.k, sh, cs, [&](int e) { return idx[e]; },
+                 [&](uint32_t pos, uint32_t, int32_t i) { out[pos] = i; });
 }
 
-// Key-block length for the blocked mode, or 0 for one workgroup per row.
+// Key-block length for the blocked mode, or 0 for one workgroup per row. A few rows of
+// up to 32,768 keys still take the blocked mode: one workgroup alone streams a long row
+// from HBM and selects in it more slowly than many workgroups select in its blocks
+// and a second launch merges their candidates.
 static int pick_block(int32_t n_rows, int64_t ld, int32_t k) {
   if (ld <= 4096 || (ld <= 32768 && n_rows >= 128)) return 0;
   // few long rows: blocks of 4,096 .. 32,768 keys so that about 64 workgroups run,
-  // with the merged candidates (blocks x k) at most 32,768
+  // with the merged candidates (blocks x kp) at most 32,768
+  const int64_t kp = (k + 3) / 4 * 4;
   int64_t B = 4096;
   while (B < 32768 && n_rows * ((ld + B - 1) / B) > 64) B *= 2;
-  while (B < 32768 && ((ld + B - 1) / B) * k > 32768) B *= 2;
-  if (((ld + B - 1) / B) * k > 32768) return -1;
+  while (B < 32768 && ((ld + B - 1) / B) * kp > 32768) B *= 2;
+  if (((ld + B - 1) / B) * kp > 32768) return -1;
   return (int)B;
 }
 
@@ -331,7 +448,8 @@ size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k) {
   if (B < 0) return (size_t)-1;
   if (B == 0) return 0;
   const int64_t nb = (ld + B - 1) / B;
-  return (size_t)n_rows * nb * k * 8;
+  const int64_t kp = (k + 3) / 4 * 4;
+  return (size_t)n_rows * nb * kp * 8;
 }
 
 template <int E>
@@ -362,6 +480,8 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   a.n_valid = n_valid;
   a.k = k;
   a.blocks = blocks;
+  a.vec = ld % 4 == 0 && ((uintptr_t)logits & 15) == 0;
+  a.kp = (k + 3) / 4 * 4;
   const int B = pick_block(n_rows, ld, k);
   if (B == 0) {
     a.blk = (int)ld;
@@ -380,7 +500,7 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   a.blk = B;
   a.nblk = (int32_t)nb;
   a.ws_key = (uint32_t*)ws;
-  a.ws_idx = (int32_t*)((char*)ws + (size_t)n_rows * nb * k * 4);
+  a.ws_idx = (int32_t*)((char*)ws + (size_t)n_rows * nb * a.kp * 4);
   if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_topk_blocks: at most 65535 rows in blocked mode");
   switch (run_for(B)) {
     case 4: launch_stage1<4>(a, st); break;
@@ -390,7 +510,7 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   }
   tf_status s = launch_status("tf_topk_blocks");
   if (s != TF_OK) return s;
-  switch (run_for(nb * k)) {
+  switch (run_for(nb * a.kp)) {
     case 4: launch_stage2<4>(a, st); break;
     case 8: launch_stage2<8>(a, st); break;
     case 16: launch_stage2<16>(a, st); break;

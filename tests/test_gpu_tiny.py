@@ -231,6 +231,32 @@ def test_topk_edge_cases():
     assert np.array_equal(host(blk), np.tile(np.arange(512), (2, 1)))
 
 
+def test_topk_sampled_threshold_paths():
+    """Rows of 16 and 32 keys per thread cut their keys down with a threshold from
+    per-group maxima (1, 2 or 4 samples per thread as k grows) before the exact
+    selection; ragged rows, few visible samples, heavy ties (the whole-row fallback)
+    and continuous values all give the exact top-k."""
+    _log("top-k: sampled thresholds, k up to 2048, fallbacks")
+    rng = np.random.default_rng(13)
+    for ld, k, ties in [(20000, 512, False), (20000, 1000, False), (30000, 1500, False), (32768, 2048, False),
+                        (10000, 700, False), (20000, 512, True), (32768, 2048, True)]:
+        R = 130                                                    # >= 128 rows: one workgroup per row
+        v = rng.standard_normal((R, ld)).astype(np.float32)
+        if ties:
+            v = np.round(v, 1).astype(np.float32)
+        nv = rng.integers(k + 1, ld + 1, size=R).astype(np.int32)
+        nv[0] = ld
+        nv[1] = k + 1                                              # fewer valid samples than k
+        nv[2] = k
+        nv[3] = 1
+        lg = torch.from_numpy(v).cuda()
+        nvt = torch.from_numpy(nv).cuda()
+        blk = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        tf.topk_blocks(lg, nvt, k, blk)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(blk), topk_on_values(v, nv, k)), (ld, k, ties)
+
+
 def test_topk_blocked_workspace_reuse_and_graph_replay():
     """Long rows merge per-block candidates through the workspace: a reused workspace,
     a workspace of arbitrary bytes and replays of a captured call all give the exact
