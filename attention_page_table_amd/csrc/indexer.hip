@@ -45,10 +45,22 @@ struct IdxArgs {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// max(x, 0) as one v_med3_f32 (the median of x, 0 and +inf). fmaxf would first
-// quiet a signaling NaN with one more instruction per value; here a NaN gives 0
-// either way.
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); }
+// max(x, 0) as one integer max on the bits: a float with the sign bit set (negative,
+// -0) is a negative int32 and becomes +0; a non-negative float keeps its bits. A float
+// max would first quiet signaling NaNs, one more instruction per value.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
+}
+
+// sum_h w[h] * ReLU(acc[h]) over N values, in four independent chains so that the
+// dependent FMAs do not serialize
+template <int N, typename A>
+__device__ __forceinline__ float weighted_relu_sum(const float* w, const A& acc, int off) {
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < N; ++h) s[h & 3] = __builtin_fmaf(w[h], relu(acc[off + h]), s[h & 3]);
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
 
 __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
   const int pos = a.row_pos[row];
@@ -112,9 +124,7 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
     for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], cur[ks], acc, 0, 0, 0);
     const int pg = page_at(kt);
     if (kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < H; ++i) s = __builtin_fmaf(wv[i], relu(acc[i]), s);
+    const float s = weighted_relu_sum<H>(wv, acc, 0);
     const int64_t key = kt + n;
     if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
   };
@@ -310,9 +320,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
       for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[t][ks], bfrag[ks], acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < RH; ++r) {
-        float s = 0.f;
-#pragma unroll
-        for (int h = 0; h < H; ++h) s = __builtin_fmaf(wv[t][r * H + h], relu(acc[r * H + h]), s);
+        const float s = weighted_relu_sum<H>(&wv[t][r * H], acc, r * H);
         if (M == kOpen) {
           optr[t][r][kt] = s;
         } else {
