@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=6, help="pool copies rotated between steps")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=5, help="timed passes of the whole prefill-chunk step")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length")
     ap.add_argument("--summarize-trace", metavar="DB")
@@ -273,7 +274,7 @@ def main():
                 "avg_launch_us": round(avg_ms[dom] * 1e3, 2)}
 
     # ------------------------------------------------------------------ prefill indexer
-    prefill = None
+    prefill = prefill_step = None
     if not args.no_prefill:
         del launches, views, pools, P0
         torch.cuda.empty_cache()
@@ -306,6 +307,7 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
                                 "traffic": load_traffic("indexer_prefill")}}
+        prefill_step = bench_prefill_step(tf, pw, pplan, PP, prs, prp, piq, pww, plog, pnv, args.prefill_reps)
         del PP, plog
 
     # ------------------------------------------------------------------ oracle on the host
@@ -327,10 +329,94 @@ def main():
         "roofline": roofline,
         "kernels": kern,
         "prefill_indexer": prefill,
+        "prefill_step": prefill_step,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
+    """The whole hot path over one prefill chunk (rows [97,952, 100,000) of one stream
+    against its 100,000-token prefix): write the chunk's rows and pooled keys, logits
+    over every visible key, top-512 per row, attention with 32 heads. Each call is
+    timed with fence-free events over `reps` passes; the pool is resident."""
+    import numpy as np
+    import torch
+    from synth import TAG_LATENT, TAG_PKEY, TAG_Q
+    from synth.configs import LAT, ROPE, ROW
+    from synth.device import _rid, fill_bf16
+    T = len(pw.rows)
+    t0 = pw.rows[0][1]
+    r0 = _rid(0, 0, t0)
+    lat = torch.empty((T, LAT), dtype=torch.bfloat16, device="cuda")
+    rope = torch.empty((T, ROPE), dtype=torch.bfloat16, device="cuda")
+    fill_bf16(lat, T, LAT, pw.seed, TAG_LATENT, r0 * ROW, ROW, ROW)
+    fill_bf16(rope, T, ROPE, pw.seed, TAG_LATENT, r0 * ROW + LAT, ROW, ROW)
+    j0, j1 = (t0 + 3) // 4, (t0 + T + 3) // 4
+    keys = torch.empty((j1 - j0, pw.Dk), dtype=torch.bfloat16, device="cuda")
+    fill_bf16(keys, j1 - j0, pw.Dk, pw.seed, TAG_PKEY, _rid(0, 0, j0) * pw.Dk, pw.Dk, pw.Dk)
+    ks = torch.zeros(j1 - j0, dtype=torch.int32, device="cuda")
+    ki = torch.arange(j0, j1, dtype=torch.int32, device="cuda")
+    q = torch.empty((T, pw.Hq, ROW), dtype=torch.bfloat16, device="cuda")
+    fill_bf16(q, T * pw.Hq, ROW, pw.seed, TAG_Q, r0 * pw.Hq * ROW, ROW, ROW)
+    blocks = torch.empty((T, pw.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, pw.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, pw.Hq), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(576.0)
+    view = PP.view()
+    calls = [
+        ("write", tf.latent_write(plan, view, rs, rp, lat, rope, pkey_stream=ks, pkey_idx=ki, pkeys=keys,
+                                  prepare=True)),
+        ("indexer", tf.indexer_logits(plan, view, rs, rp, iq, w, logits, n_valid=nv, prepare=True)),
+        ("topk", tf.topk_blocks(logits, nv, pw.k, blocks, prepare=True)),
+        ("attention", tf.sparse_mla_attn(plan, view, rs, rp, q, scale, blocks, out, lse, prepare=True)),
+    ]
+    for _, f in calls:
+        f()
+    torch.cuda.synchronize()
+    ev = [[TimingEvent() for _ in range(len(calls) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        for c, (_, f) in enumerate(calls):
+            f()
+            ev[i][c + 1].record()
+    torch.cuda.synchronize()
+    us = {n: float(np.mean([ev[i][c].elapsed_time(ev[i][c + 1]) for i in range(reps)])) * 1e3
+          for c, (n, _) in enumerate(calls)}
+    step_us = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(reps)])) * 1e3
+    nvh = nv.cpu().numpy().astype(np.int64)
+    blk = blocks.cpu().numpy()
+    sel = 0
+    for r, (_, t) in enumerate(pw.rows):                               # exact: tokens s <= t of the selected blocks
+        b = blk[r][blk[r] >= 0].astype(np.int64)
+        sel += int(np.minimum(4, np.maximum(0, t + 1 - 4 * b)).sum())
+    attn_flop = sel * 4 * pw.Hq * 576
+    idx_flop = int(sum(2 * pw.H * pw.Dk * int(n) for n in nvh))
+    def mfma(flop, t_us):
+        a = flop / (t_us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+    def hbm(nbytes, t_us):
+        a = nbytes / (t_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
+    res = {
+        "workload": pw.name, "rows": T, "keys": int(logits.shape[1]), "topk_blocks": pw.k, "attn_heads": pw.Hq,
+        "us_per_step": round(step_us, 1), "reps": reps,
+        "calls": {
+            "write": {"us": round(us["write"], 2),
+                      "roofline": hbm(2 * (T * ROW_BYTES + (j1 - j0) * pw.Dk * 2), us["write"])},
+            "indexer": {"us": round(us["indexer"], 2), "causal_flop": idx_flop,
+                        "roofline": mfma(idx_flop, us["indexer"])},
+            "topk": {"us": round(us["topk"], 2), "roofline": hbm(int(logits.numel()) * 4, us["topk"])},
+            "attention": {"us": round(us["attention"], 2), "selected_tokens": sel, "flop": attn_flop,
+                          "gathered_bytes": sel * ROW_BYTES,
+                          "gathered_GBps": round(sel * ROW_BYTES / (us["attention"] * 1e-6) / 1e9, 1),
+                          "roofline": mfma(attn_flop, us["attention"])},
+        },
+    }
+    return res
 
 
 def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
