@@ -52,14 +52,14 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
 }
 
-// sum_h w[h] * ReLU(acc[h]) over N values, in four independent chains so that the
-// dependent FMAs do not serialize
+// sum_h w[h] * ReLU(acc[h]) over N values, in two independent chains so that
+// consecutive FMAs do not wait on each other
 template <int N, typename A>
 __device__ __forceinline__ float weighted_relu_sum(const float* w, const A& acc, int off) {
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float s[2] = {0.f, 0.f};
 #pragma unroll
-  for (int h = 0; h < N; ++h) s[h & 3] = __builtin_fmaf(w[h], relu(acc[off + h]), s[h & 3]);
-  return (s[0] + s[1]) + (s[2] + s[3]);
+  for (int h = 0; h < N; ++h) s[h & 1] = __builtin_fmaf(w[h], relu(acc[off + h]), s[h & 1]);
+  return s[0] + s[1];
 }
 
 __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
@@ -278,17 +278,28 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   // 128): 32 * CH pieces of 16 bytes per subtile, 64 per wave-wide load; the lane that
   // fills swizzled position p loads the piece that belongs there. Keys past kend in
   // the chunk are read too (same page) and masked when scored.
-  auto issue = [&](int64_t kt, __bf16* dst) __attribute__((always_inline)) {
-    const int pg = pg_lds[(int)(kt / kKeysPerPage) - p0];
-    const char* base = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey : nullptr;
+  // The pieces a lane loads sit at the same offsets in every chunk: the lane's offsets
+  // within a subtile are computed once (one or two of them), the subtile's start joins
+  // the scalar base, and each load is a scalar base plus a vector offset.
+  constexpr int kRowsPerSub = CH * 32 / 64;   // wave-wide loads per subtile
+  constexpr int kPar = kRowsPerSub / 4;       // distinct in-subtile offsets per lane
+  uint32_t dma_off[kPar];
 #pragma unroll
-    for (int i = wave; i < CH * kChunk / 64; i += 4) {
-      const int p = i * 64 + lane;
-      const int sub = p / (CH * 32), q = p % (CH * 32);
-      const int j = q / CH, c = (q % CH) ^ (j & (CH - 1));
-      const char* src = base ? base + (int64_t)(sub * 32 + j) * a.pkey_row_bytes + c * 16
-                             : a.v.pool + c * 16;   // any readable bytes: rows of a missing page become NaN
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&dst[i * 64 * 8], 16, 0, 0);
+  for (int pp = 0; pp < kPar; ++pp) {
+    const int q = (wave + 4 * pp) * 64 + lane;
+    const int j = q / CH, c = (q % CH) ^ (j & (CH - 1));
+    dma_off[pp] = (uint32_t)(j * a.pkey_row_bytes + c * 16);
+  }
+  auto issue = [&](int64_t kt, __bf16* dst) __attribute__((always_inline)) {
+    const int pg = __builtin_amdgcn_readfirstlane(pg_lds[(int)(kt / kKeysPerPage) - p0]);
+    // a missing page reads any readable bytes: its keys' logits are written as NaN
+    const char* base = pg >= 0 ? cache_block(a.v, pg) + a.off_pkey : a.v.pool;
+#pragma unroll
+    for (int u = 0; u < CH / 2; ++u) {
+      const int i = wave + 4 * u;
+      const char* bu = base + (int64_t)(u / kPar) * 32 * a.pkey_row_bytes;
+      __builtin_amdgcn_global_load_lds((const void*)(bu + dma_off[u % kPar]), (lds_void*)&dst[i * 64 * 8], 16, 0,
+                                       0);
     }
   };
 

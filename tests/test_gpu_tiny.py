@@ -149,6 +149,22 @@ def test_decode_rows_split_paths(tiny_pool, hq):
     check_attention(out, lse, ro, rl, "decode split")
 
 
+@pytest.mark.parametrize("scale", SCALES)
+def test_prefill_rows_split_and_sparse_tiles(tiny_pool, scale):
+    """Many rows with 32 heads (one workgroup per row and split, all heads together):
+    154 rows split each block list in two (partials and the merge kernel); rows near
+    the start of a stream have fewer visible blocks than k, so whole tiles hold no
+    attended token."""
+    _log(f"prefill rows: 32 heads, split block lists, sparse tiles, scale {scale:.4f}")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, 32)
+    rows = [(0, t) for t in range(1792, 1792 + 150)] + [(1, 3), (1, 40), (0, 511), (1, 2047)]
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, 512, scale)
+    assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+    ro, rl = ow.attention(wl, 0, rows, blk, scale)
+    check_attention(out, lse, ro, rl, "prefill rows")
+
+
 def test_paged_equals_contiguous_bitwise(tiny_pool):
     _log("paged == contiguous window, bit for bit (tiny)")
     wl, plan, P = tiny_pool
