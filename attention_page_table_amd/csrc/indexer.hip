@@ -305,61 +305,82 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 
   const float ninf = -__builtin_inff();
   const float qnan = __builtin_nanf("");
-  // One 32-key subtile: B fragments from LDS, MT x KS MFMAs, the head sum, the
-  // stores. Subtiles past kend are computed too (their keys are in the chunk's page)
-  // and only keys < ke are stored. Modes: kOpen, every key of the chunk is stored
-  // and visible to every row (no selects); kFull, every key is stored; kPart, keys
-  // are tested against ke.
+  // A chunk is four 32-key subtiles of MT tiles each. Tile (sub, t) accumulates into
+  // acc[t]; its head sum and stores run while the next tile's MFMAs do (four VALU
+  // instructions between consecutive MFMAs), so the two accumulators alternate and
+  // the vector ALU works beside the matrix core (kPipe; with 128-dim keys and fewer
+  // than 16 heads a lane holds several rows and the registers do not suffice, so
+  // each tile's head sum follows its MFMAs there). The next subtile's B fragments are
+  // read from LDS during the last tile's MFMAs, each right after its register is
+  // consumed. Subtiles past kend are computed too (their keys are in the chunk's
+  // page) and only keys < ke are stored. Modes: kOpen, every key of the chunk is
+  // stored and visible to every row (no selects); kFull, every key is stored; kPart,
+  // keys are tested against ke.
   constexpr int kOpen = 0, kFull = 1, kPart = 2;
-  auto subtile = [&](int64_t kt, const __bf16* src, bool pg_ok, auto mode) __attribute__((always_inline)) {
+  constexpr int kSubs = kChunk / 32;
+  constexpr bool kPipe = H == 16 || D == 64;
+  auto epilogue = [&](const f32x16& acc, int t, int64_t kt, bool pg_ok, auto mode) __attribute__((always_inline)) {
     constexpr int M = decltype(mode)::value;
+    const int64_t key = kt + n;
+#pragma unroll
+    for (int r = 0; r < RH; ++r) {
+      const float s = weighted_relu_sum<H>(&wv[t][r * H], acc, r * H);
+      if (M == kOpen) {
+        optr[t][r][kt] = s;
+      } else {
+        const float v = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
+        if (M == kFull || key < ke) optr[t][r][kt] = v;
+      }
+    }
+  };
+  auto chunk_body = [&](int64_t kt0, const __bf16* src, bool pg_ok, auto mode) __attribute__((always_inline)) {
+    f32x16 acc[MT];
     bf16x8 bfrag[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bfrag[ks] = *(const bf16x8*)&src[swz<CH>(n, 2 * ks + g) * 8];
-    const int64_t key = kt + n;
-    // B reads interleaved with the first MFMAs: four reads, then one read per two MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
 #pragma unroll
-    for (int i = 0; i < KS / 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const int64_t kt = kt0 + sub * 32;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      f32x16 acc = {};
+      for (int t = 0; t < MT; ++t) {
+        acc[t] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[t][ks], bfrag[ks], acc, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[t][ks], bfrag[ks], acc[t], 0, 0, 0);
+          if (t == MT - 1 && sub + 1 < kSubs)
+            bfrag[ks] = *(const bf16x8*)&src[(sub + 1) * 32 * D + swz<CH>(n, 2 * ks + g) * 8];
+        }
+        if constexpr (kPipe) {
+          if (t > 0) epilogue(acc[t - 1], t - 1, kt, pg_ok, mode);
+          else if (sub > 0) epilogue(acc[MT - 1], MT - 1, kt - 32, pg_ok, mode);
+          // pin the interleave: per MFMA, the B read that refills its register (last
+          // tile only) and four instructions of the previous tile's head sum
 #pragma unroll
-      for (int r = 0; r < RH; ++r) {
-        const float s = weighted_relu_sum<H>(&wv[t][r * H], acc, r * H);
-        if (M == kOpen) {
-          optr[t][r][kt] = s;
+          for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (t == MT - 1 && sub + 1 < kSubs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (t > 0 || sub > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
         } else {
-          const float v = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
-          if (M == kFull || key < ke) optr[t][r][kt] = v;
+          epilogue(acc[t], t, kt, pg_ok, mode);
         }
       }
     }
+    if constexpr (kPipe) epilogue(acc[MT - 1], MT - 1, kt0 + (kSubs - 1) * 32, pg_ok, mode);
   };
   // which mode a chunk runs in, and the vector-memory operations it issues after the
   // next chunk's loads (its stores), so that the next barrier waits for the loads only
   auto chunk = [&](int64_t kt, const __bf16* src) __attribute__((always_inline)) -> bool {
     const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
     if (kt + kChunk <= ke && pg_ok && kt + kChunk <= nc_min) {
-#pragma unroll
-      for (int sub = 0; sub < kChunk / 32; ++sub)
-        subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kOpen>{});
+      chunk_body(kt, src, pg_ok, std::integral_constant<int, kOpen>{});
       return true;
     }
     if (kt + kChunk <= ke) {
-#pragma unroll
-      for (int sub = 0; sub < kChunk / 32; ++sub)
-        subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kFull>{});
+      chunk_body(kt, src, pg_ok, std::integral_constant<int, kFull>{});
       return true;
     }
-#pragma unroll
-    for (int sub = 0; sub < kChunk / 32; ++sub)
-      subtile(kt + sub * 32, src + sub * 32 * D, pg_ok, std::integral_constant<int, kPart>{});
+    chunk_body(kt, src, pg_ok, std::integral_constant<int, kPart>{});
     return false;
   };
   // Wait for this wave's loads of the chunk about to be published. After a chunk
