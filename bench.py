@@ -50,13 +50,18 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 512 * 2 + 64 * 2
 CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
 
-# entry point -> (kernels it launches, by name prefix; source file)
+# entry point -> (kernels it launches, by name prefix; source file). The decode step's
+# calls and the prefill chunk's launch different kernels for top-k and attention, so
+# they are separate entries; the latent write is one kernel in both (its decode grid is
+# the one launched most often).
 ENTRIES = {
     "write": (("tf::latent_write_kernel",), "write.hip"),
     "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
     "indexer_prefill": (("tf::indexer_tile_kernel",), "indexer.hip"),
-    "topk": (("tf::topk_stage1_kernel", "tf::topk_stage2_kernel", "tf::topk_row_kernel"), "topk.hip"),
-    "attention": (("tf::attn_decode_kernel", "tf::attn_kernel", "tf::attn_merge_kernel"), "attention.hip"),
+    "topk": (("tf::topk_stage1_kernel", "tf::topk_stage2_kernel"), "topk.hip"),
+    "topk_prefill": (("tf::topk_row_kernel",), "topk.hip"),
+    "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
+    "attention_prefill": (("tf::attn_kernel",), "attention.hip"),
 }
 TRAFFIC_FILE = "traffic_bench_decode_8x131072_prefill_indexer_2048_at_100000.json"
 CAL_KERNEL = "neg_kernel"      # torch.neg over CAL_BYTES of float32: a plain streaming copy
@@ -531,6 +536,9 @@ def summarize_trace(db, label, command, bench_json=None):
         ev = {n: d["us"] for n, d in b["kernels"].items()}
         if b.get("prefill_indexer"):
             ev["indexer_prefill"] = b["prefill_indexer"]["us"]
+        for call, e in (("topk", "topk_prefill"), ("attention", "attention_prefill")):
+            if b.get("prefill_step"):
+                ev[e] = b["prefill_step"]["calls"][call]["us"]
         for e, us in ev.items():
             k = sum(a for _, _, a in per_entry.get(e, []))
             lines.append(f"{e:16s} events {us:9.2f} us   kernels {k:9.2f} us   ratio {us / k if k else 0:.3f}")
