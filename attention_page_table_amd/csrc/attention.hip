@@ -58,10 +58,17 @@ struct AttnArgs {
   float* part_ml;  // [n_rows][nsplit][32][2]  (max in log2 domain, sum)
 };
 
+// Row stride of the partial S tiles in floats: 16-byte aligned rows (vector reads in
+// the softmax), and the rows one MFMA store instruction writes land on disjoint LDS
+// banks (32x32 tiles: the two half-waves' rows are 4 apart, 4 x 40 = 32 banks mod 64;
+// 16x16 tiles: the four lane groups' rows are 4 apart, 4 x 36 = 16 banks mod 64).
+template <int HG>
+constexpr int kSpartStride = HG == 32 ? kTileTok + 8 : kTileTok + 4;
+
 template <int HG>
 struct alignas(16) AttnShared {
   __bf16 kv[kTileTok][kRS];
-  float spart[HG == 32 ? 4 : 2][HG][kTileTok + 1];
+  float spart[HG == 32 ? 4 : 2][HG][kSpartStride<HG>];
   __bf16 p_hi[HG][kTileTok + 8];
   __bf16 p_lo[HG][kTileTok + 8];
   float tsc[kTileTok];         // per-token value scale of the current tile (fp8)
@@ -268,16 +275,21 @@ template <int HG, int NPARTS, bool FP8, typename SH>
 __device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const float* tsc, float scale_log2, int tid) {
   constexpr int TPH = 256 / HG, TPT = kTileTok / TPH;
   const int h = tid / TPH, p = tid % TPH;
+  // this thread's TPT consecutive tokens: one vector read per partial tile and one
+  // of the token table (the partials summed in the same order as one at a time)
+  typedef float fv_t __attribute__((ext_vector_type(TPT)));
+  typedef int32_t iv_t __attribute__((ext_vector_type(TPT)));
+  typedef __bf16 bv_t __attribute__((ext_vector_type(TPT)));
+  fv_t sv = *(const fv_t*)&sh.spart[0][h][p * TPT];
+#pragma unroll
+  for (int pp = 1; pp < NPARTS; ++pp) sv += *(const fv_t*)&sh.spart[pp][h][p * TPT];
+  const iv_t tv = *(const iv_t*)&tt[p * TPT];
   float z[TPT];
   float tmax = -__builtin_inff();
 #pragma unroll
   for (int e = 0; e < TPT; ++e) {
-    const int tok = p * TPT + e;
-    float v = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < NPARTS; ++pp) v += sh.spart[pp][h][tok];
-    v *= scale_log2;
-    if (tt[tok] < 0) v = -__builtin_inff();   // not attended
+    float v = sv[e] * scale_log2;
+    if (tv[e] < 0) v = -__builtin_inff();   // not attended
     z[e] = v;
     tmax = __builtin_fmaxf(tmax, v);
   }
@@ -286,6 +298,7 @@ __device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const fl
   const float m_new = __builtin_fmaxf(m_old, tmax);
   const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_old - m_new);
   float lsum = 0.f;
+  bv_t phv, plv;
 #pragma unroll
   for (int e = 0; e < TPT; ++e) {
     const int tok = p * TPT + e;
@@ -293,9 +306,11 @@ __device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const fl
     lsum += pe;
     const float pv = FP8 ? pe * tsc[tok] : pe;
     const __bf16 hi = bf16_rne(pv);
-    sh.p_hi[h][tok] = hi;
-    sh.p_lo[h][tok] = bf16_rne(pv - bf16_to_f(hi));
+    phv[e] = hi;
+    plv[e] = bf16_rne(pv - bf16_to_f(hi));
   }
+  *(bv_t*)&sh.p_hi[h][p * TPT] = phv;
+  *(bv_t*)&sh.p_lo[h][p * TPT] = plv;
   lsum = group_sum<TPH>(lsum);
   __syncthreads();  // every thread of the head has read m_run
   if (p == 0) {
