@@ -54,7 +54,7 @@ typedef enum {
   TF_E_INVAL = 1,        /* an argument is malformed */
   TF_E_RANGE = 2,        /* a size or index is out of the supported range */
   TF_E_NOMEM = 3,        /* the plan's room cannot fund one window (refused at start) */
-  TF_E_UNSUPPORTED = 4,  /* a shape this build has no kernel for */
+  TF_E_UNSUPPORTED = 4,  /* a shape the library has no kernel for */
   TF_E_DEVICE = 5        /* the HIP runtime reported an error */
 } tf_status;
 
