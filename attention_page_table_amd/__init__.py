@@ -54,6 +54,8 @@ SIGNATURES = {
     "tf_prefill_chunk": (_c_i64, [_c_i64, _c_i64]),
     "tf_latent_write": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i32,
                                  _vp, _vp, _vp, _vp]),
+    "tf_latent_write_quantize": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp,
+                                          _c_i32, _vp, _vp, _vp, _vp]),
     "tf_indexer_logits": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32, _vp,
                                    _c_i64, _vp, _vp]),
     "tf_topk_blocks": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -171,6 +173,16 @@ def latent_write(plan, dst, row_stream, row_pos, latent, rope, row_scale=None,
     return _run("tf_latent_write", (ctypes.byref(plan), dst, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(latent),
                                     _ptr(row_scale), _ptr(rope), n_pk, _ptr(pkey_stream), _ptr(pkey_idx),
                                     _ptr(pkeys), _stream(stream)), prepare)
+
+
+def latent_write_quantize(plan, dst, row_stream, row_pos, latent, rope, pkey_stream=None, pkey_idx=None,
+                          pkeys=None, stream=None, prepare=False):
+    """bf16 latent rows coded as e4m3 with a row scale on the device (fp8 plans only)."""
+    n_rows = 0 if row_stream is None else row_stream.numel()
+    n_pk = 0 if pkey_stream is None else pkey_stream.numel()
+    return _run("tf_latent_write_quantize", (ctypes.byref(plan), dst, n_rows, _ptr(row_stream), _ptr(row_pos),
+                                             _ptr(latent), _ptr(rope), n_pk, _ptr(pkey_stream), _ptr(pkey_idx),
+                                             _ptr(pkeys), _stream(stream)), prepare)
 
 
 def indexer_logits(plan, keys, row_stream, row_pos, q, w, logits, n_valid=None, stream=None, prepare=False):

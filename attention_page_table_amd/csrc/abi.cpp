@@ -94,7 +94,38 @@ extern "C" tf_status tf_latent_write(const tf_plan* p, tf_kv_view dst, int32_t n
   }
   if (n_rows == 0 && n_pkeys == 0) return TF_OK;
   return launch_latent_write(p, make_view(p, dst), n_rows, row_stream, row_pos, latent, row_scale, rope,
-                             n_pkeys, pkey_stream, pkey_idx, pkeys, (hipStream_t)stream);
+                             n_pkeys, pkey_stream, pkey_idx, pkeys, (hipStream_t)stream, false);
+}
+
+extern "C" tf_status tf_latent_write_quantize(const tf_plan* p, tf_kv_view dst, int32_t n_rows,
+                                              const int32_t* row_stream, const int32_t* row_pos,
+                                              const void* latent, const void* rope, int32_t n_pkeys,
+                                              const int32_t* pkey_stream, const int32_t* pkey_idx,
+                                              const void* pkeys, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if (p->g.lat_fmt != TF_LAT_FP8E4M3_ROWSCALE)
+    return set_error(TF_E_INVAL,
+                     "tf_latent_write_quantize: the plan's rows are bf16; plan with lat_fmt "
+                     "TF_LAT_FP8E4M3_ROWSCALE, or write bf16 rows with tf_latent_write");
+  if ((s = check_view(p, dst, "dst")) != TF_OK) return s;
+  if (n_rows < 0 || n_pkeys < 0) return set_error(TF_E_INVAL, "tf_latent_write_quantize: negative counts");
+  if (n_rows > 0) {
+    if (!row_stream || !row_pos || !latent)
+      return set_error(TF_E_INVAL, "tf_latent_write_quantize: row_stream, row_pos and latent are required");
+    if (p->g.rope_dim > 0 && !rope) return set_error(TF_E_INVAL, "tf_latent_write_quantize: rope is required");
+    if (!aligned16(latent) || (rope && !aligned16(rope)))
+      return set_error(TF_E_INVAL, "tf_latent_write_quantize: latent and rope must be 16-byte aligned");
+  }
+  if (n_pkeys > 0) {
+    if (!pkey_stream || !pkey_idx || !pkeys)
+      return set_error(TF_E_INVAL, "tf_latent_write_quantize: pkey_stream, pkey_idx and pkeys are required");
+    if (!aligned16(pkeys)) return set_error(TF_E_INVAL, "tf_latent_write_quantize: pkeys must be 16-byte aligned");
+  }
+  if (n_rows == 0 && n_pkeys == 0) return TF_OK;
+  return launch_latent_write(p, make_view(p, dst), n_rows, row_stream, row_pos, latent, nullptr, rope, n_pkeys,
+                             pkey_stream, pkey_idx, pkeys, (hipStream_t)stream, true);
 }
 
 extern "C" tf_status tf_snapshot_copy(const tf_plan* p, tf_kv_view src, tf_kv_view dst,

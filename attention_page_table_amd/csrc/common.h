@@ -56,7 +56,7 @@ tf_status launch_latent_write(const tf_plan* p, const DevView& v, int32_t n_rows
                               const int32_t* row_stream, const int32_t* row_pos,
                               const void* latent, const float* row_scale, const void* rope,
                               int32_t n_pkeys, const int32_t* pkey_stream, const int32_t* pkey_idx,
-                              const void* pkeys, hipStream_t st);
+                              const void* pkeys, hipStream_t st, bool quantize);
 tf_status launch_snapshot(const tf_plan* p, const tf_kv_view& src, const tf_kv_view& dst,
                           int32_t n_streams, const int32_t* src_stream, const int32_t* dst_stream,
                           int64_t at, hipStream_t st);

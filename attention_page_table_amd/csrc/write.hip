@@ -1,5 +1,6 @@
 // Latent / rope / pooled-key row writes through the page table, and the snapshot
-// copy of a stream's first `at` rows. Both are byte copies, bound by HBM.
+// copy of a stream's first `at` rows. Both are byte copies, bound by HBM; the
+// quantizing write turns bf16 latent rows into e4m3 codes and a row scale on the way.
 //
 // [#1142, "GLM declares a kv_pool.Layout"]: the writes take the page table; a
 // null table keeps contiguous rows. [#1142, "Proposal" piece 1]: a kept state
@@ -23,10 +24,58 @@ struct WriteArgs {
   int64_t off_scale, off_rope, off_pkey;
   int32_t lat_row_bytes, rope_row_bytes, pkey_row_bytes;
   int32_t row_blocks;    // blocks that write rows; the rest write keys
+  int32_t quantize;      // latent holds bf16 rows to code as e4m3 with a row scale
 };
 
 constexpr int kRowsPerBlock = 4;   // 64 threads per row
 constexpr int kKeysPerBlock = 16;  // 16 threads per key
+
+// e4m3fn code of q, |q| <= 448 (a finite value already clamped), rounding to nearest
+// with ties to the even code. Below 2^-6 the codes step by 2^-9 (subnormals, and
+// code 8 = 2^-6 continues them). Above, the fp32 mantissa is rounded to 3 bits
+// (ties to even) and the exponent rebiased from 127 to 7; the clamp keeps the result
+// at or below 0x7E (448), never the NaN code 0x7F. The sign comes from q's sign bit.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t bits = __float_as_uint(q);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t mag = bits & 0x7FFFFFFFu;
+  uint32_t code;
+  if (mag < 0x3C800000u) {   // |q| < 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  } else {
+    code = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// One wave codes one 512-value row: lane l holds values 8l .. 8l+7 (16 bytes of
+// bf16), the wave's max |x| gives scale = amax / 448, and the lane writes its 8
+// codes as 8 contiguous bytes; lane 0 writes the scale.
+__device__ __forceinline__ void quantize_row(const uint4* src, uint8_t* dst_codes, float* dst_scale, int lane) {
+  const uint4 v = src[lane];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float scale = amax / 448.0f;
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q = scale > 0.f ? x[i] / scale : 0.f;
+    q = __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
+    c[i >> 2] |= e4m3_code(q) << (8 * (i & 3));
+  }
+  *(uint2*)(dst_codes + 8 * lane) = make_uint2(c[0], c[1]);
+  if (lane == 0) *dst_scale = scale;
+}
 
 __global__ __launch_bounds__(256) void latent_write_kernel(WriteArgs a) {
   const int tid = threadIdx.x;
@@ -41,9 +90,14 @@ __global__ __launch_bounds__(256) void latent_write_kernel(WriteArgs a) {
     if (page < 0) return;
     char* blk = cache_block(a.v, page);
     const int slot = t % kPageRows;
-    uint4* dl = (uint4*)(blk + (int64_t)slot * a.lat_row_bytes);
-    const uint4* sl = a.latent + (int64_t)r * a.lat16;
-    for (int i = lane; i < a.lat16; i += 64) dl[i] = sl[i];
+    if (a.quantize) {
+      quantize_row(a.latent + (int64_t)r * (kLatent * 2 / 16), (uint8_t*)(blk + (int64_t)slot * a.lat_row_bytes),
+                   (float*)(blk + a.off_scale + 4LL * slot), lane);
+    } else {
+      uint4* dl = (uint4*)(blk + (int64_t)slot * a.lat_row_bytes);
+      const uint4* sl = a.latent + (int64_t)r * a.lat16;
+      for (int i = lane; i < a.lat16; i += 64) dl[i] = sl[i];
+    }
     if (a.rope16 > 0) {
       uint4* dr = (uint4*)(blk + a.off_rope + (int64_t)slot * a.rope_row_bytes);
       const uint4* sr = a.rope + (int64_t)r * a.rope16;
@@ -69,15 +123,16 @@ tf_status launch_latent_write(const tf_plan* p, const DevView& v, int32_t n_rows
                               const int32_t* row_stream, const int32_t* row_pos, const void* latent,
                               const float* row_scale, const void* rope, int32_t n_pkeys,
                               const int32_t* pkey_stream, const int32_t* pkey_idx, const void* pkeys,
-                              hipStream_t st) {
+                              hipStream_t st, bool quantize) {
   WriteArgs a;
+  a.quantize = quantize ? 1 : 0;
   a.v = v;
   a.n_rows = n_rows;
   a.n_pkeys = n_pkeys;
   a.row_stream = row_stream;
   a.row_pos = row_pos;
   a.latent = (const uint4*)latent;
-  a.scale = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE ? row_scale : nullptr;
+  a.scale = p->g.lat_fmt == TF_LAT_FP8E4M3_ROWSCALE && !quantize ? row_scale : nullptr;
   a.rope = (const uint4*)rope;
   a.pkey_stream = pkey_stream;
   a.pkey_idx = pkey_idx;
@@ -94,7 +149,7 @@ tf_status launch_latent_write(const tf_plan* p, const DevView& v, int32_t n_rows
   a.row_blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int key_blocks = (n_pkeys + kKeysPerBlock - 1) / kKeysPerBlock;
   hipLaunchKernelGGL(latent_write_kernel, dim3(a.row_blocks + key_blocks), dim3(256), 0, st, a);
-  return launch_status("tf_latent_write");
+  return launch_status(quantize ? "tf_latent_write_quantize" : "tf_latent_write");
 }
 
 // ---- snapshot -----------------------------------------------------------------------

@@ -420,8 +420,41 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
                           "gathered_GBps": round(sel * ROW_BYTES / (us["attention"] * 1e-6) / 1e9, 1),
                           "roofline": mfma(attn_flop, us["attention"])},
         },
+        "quantizing_write": bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm),
     }
     return res
+
+
+def bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm):
+    """The same chunk's rows and keys written into fp8 pages by tf_latent_write_quantize
+    (the adaptive-prefill workload's row format: e4m3 codes and a row scale, bf16 rope):
+    a pool of just the chunk's pages, reached through a table whose other entries are
+    empty. Algorithmic bytes: the bf16 rows and keys read, the codes, scales, rope and
+    keys written."""
+    import numpy as np
+    import torch
+    plan8 = tf.kv_pool_plan(tf.geom(1, pw.Dk, fp8=True))
+    T = lat.shape[0]
+    t0 = pw.rows[0][1]
+    p0, p1 = t0 // 512, (t0 + T - 1) // 512 + 1
+    pool = torch.zeros((p1 - p0) * plan8.page_bytes, dtype=torch.uint8, device="cuda")
+    pt = torch.full((1, p1), -1, dtype=torch.int32, device="cuda")
+    pt[0, p0:p1] = torch.arange(p1 - p0, dtype=torch.int32, device="cuda")
+    view = tf.view(pool, pt, p1, p1 - p0)
+    f = tf.latent_write_quantize(plan8, view, rs, rp, lat, rope, ks, ki, keys, prepare=True)
+    f()
+    torch.cuda.synchronize()
+    ev = [TimingEvent() for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        f()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+    nk = keys.shape[0]
+    nbytes = T * (1024 + 128) + nk * pw.Dk * 2 + T * (512 + 4 + 128) + nk * pw.Dk * 2
+    return {"call": "tf_latent_write_quantize", "rows": T, "keys": nk, "us": round(us, 2), "alg_bytes": nbytes,
+            "roofline": hbm(nbytes, us)}
 
 
 def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):

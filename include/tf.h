@@ -13,8 +13,9 @@
  *   4. tf_sparse_mla_attn   absorbed-MLA softmax attention that gathers only the
  *                           selected latent rows from the pages (decode rows and
  *                           chunked-prefill rows alike);
- *   plus tf_snapshot_copy (copy only the first `at` rows of a stream) and the
- *   host-side tf_kv_pool_plan / tf_prefill_chunk.
+ *   plus tf_latent_write_quantize (step 1 for fp8 pages, quantizing bf16 rows on
+ *   the device), tf_snapshot_copy (copy only the first `at` rows of a stream) and
+ *   the host-side tf_kv_pool_plan / tf_prefill_chunk.
  *
  * Sources (web pages, by title and section):
  *   [#1142] "Proposal: GLM-5.3-Flash on CUDA takes its streams' KV pages from the
@@ -153,6 +154,27 @@ tf_status tf_latent_write(const tf_plan* p, tf_kv_view dst, int32_t n_rows,
                           const void* latent, const float* row_scale, const void* rope,
                           int32_t n_pkeys, const int32_t* pkey_stream, const int32_t* pkey_idx,
                           const void* pkeys, void* stream);
+
+/* The same write for fp8 pages, quantizing on the device [#1313, "Proposal",
+ * step 1 item 3: fp8 rows on pages, each row's fp32 scale kept after the page's
+ * rows, written through the table as the bf16 write is]. The pages fix no
+ * quantization recipe; this one is per row:
+ *   scale = amax / 448 (fp32 division; amax = max |x| over the row's 512 values),
+ *   code_i = the e4m3fn value nearest to clamp(x_i / scale, -448, 448) (fp32
+ *            division), ties to the even code, sign from the quotient (so a
+ *            negative value that rounds to zero is coded -0),
+ *   and an all-zero row gets scale 0 and +0 codes.
+ * All arithmetic is IEEE fp32 (the divisions correctly rounded). The row's element
+ * of largest magnitude is coded +-448 exactly whenever the scale is a normal fp32
+ * number.
+ *   latent: bf16 [n_rows][512], finite (non-finite values give unspecified codes)
+ *   rope, pooled keys and every other argument as in tf_latent_write.
+ * TF_E_INVAL unless the plan's format is TF_LAT_FP8E4M3_ROWSCALE. */
+tf_status tf_latent_write_quantize(const tf_plan* p, tf_kv_view dst, int32_t n_rows,
+                                   const int32_t* row_stream, const int32_t* row_pos,
+                                   const void* latent, const void* rope,
+                                   int32_t n_pkeys, const int32_t* pkey_stream, const int32_t* pkey_idx,
+                                   const void* pkeys, void* stream);
 
 /* Indexer logits [CPM, section 1]: for row r (stream row_stream[r], position
  * t = row_pos[r]) and pooled key j < n_c = min(t / 4 + 1, ld):

@@ -126,6 +126,16 @@ def test_validation_refuses_before_launch():
     nv = tf.tf_kv_view(None, None, 4, 4, 16, 0)
     assert L.tf_latent_write(ctypes.byref(p), nv, 1, fake, fake, fake, None, fake, 0, None, None, None,
                              None) == tf.TF_E_INVAL
+    # the quantizing write needs an fp8 plan, and its latent rows
+    assert L.tf_latent_write_quantize(ctypes.byref(p), v, 1, fake, fake, fake, fake, 0, None, None, None,
+                                      None) == tf.TF_E_INVAL
+    assert "TF_LAT_FP8E4M3_ROWSCALE" in L.tf_last_error().decode()
+    p8 = tf.kv_pool_plan(tf.geom(1, 64, True))
+    assert L.tf_latent_write_quantize(ctypes.byref(p8), v, 1, fake, fake, None, fake, 0, None, None, None,
+                                      None) == tf.TF_E_INVAL
+    assert "latent" in L.tf_last_error().decode()
+    assert L.tf_latent_write_quantize(ctypes.byref(p8), v, 0, None, None, None, None, 0, None, None, None,
+                                      None) == tf.TF_OK
     # bad geometry
     with pytest.raises(tf.TFError) as e:
         tf.kv_pool_plan(tf.geom(1, 96))

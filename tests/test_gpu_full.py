@@ -193,3 +193,40 @@ def test_adaptive_prefill_fp8_snapshot_resume():
     assert torch.equal(fresh[3][0][1], resumed[3][0][1])
     # no poisoned byte reached the outputs
     assert not torch.isnan(resumed[3][0][0]).any()
+
+
+def test_quantizing_write_chunk_full():
+    _log("quantizing write: a 2,048-row chunk and its 512 keys into fp8 pages, every byte against the oracle")
+    from oracle import PoolImage, Geom, quantize_rows
+    pw = prefill_chunk(0)
+    plan8 = tf.kv_pool_plan(tf.geom(1, pw.Dk, fp8=True))
+    T = len(pw.rows)
+    t0 = pw.rows[0][1]
+    p0, p1 = t0 // 512, (t0 + T - 1) // 512 + 1
+    pool = torch.empty((p1 - p0) * plan8.page_bytes, dtype=torch.uint8, device="cuda")
+    pool.view(torch.int16).fill_(NAN16)
+    pt_h = np.full((1, p1), -1, dtype=np.int32)
+    pt_h[0, p0:p1] = np.random.default_rng(4).permutation(p1 - p0)
+    pt = torch.from_numpy(pt_h).cuda()
+    rng = np.random.default_rng(8)
+    x = torch.from_numpy((rng.standard_normal((T, 512)) / 24.0).astype(np.float32)).to(torch.bfloat16)
+    rope = torch.from_numpy((rng.standard_normal((T, 64)) / 24.0).astype(np.float32)).to(torch.bfloat16)
+    j0, j1 = (t0 + 3) // 4, (t0 + T + 3) // 4
+    keys = torch.from_numpy((rng.standard_normal((j1 - j0, pw.Dk)) / 8.0).astype(np.float32)).to(torch.bfloat16)
+    rs = torch.zeros(T, dtype=torch.int32, device="cuda")
+    rp = torch.arange(t0, t0 + T, dtype=torch.int32, device="cuda")
+    ks = torch.zeros(j1 - j0, dtype=torch.int32, device="cuda")
+    kj = torch.arange(j0, j1, dtype=torch.int32, device="cuda")
+    tf.latent_write_quantize(plan8, tf.view(pool, pt, p1, p1 - p0), rs, rp, x.cuda(), rope.cuda(), ks, kj,
+                             keys.cuda())
+    torch.cuda.synchronize()
+    codes, scale = quantize_rows(x.to(torch.float32).numpy())
+    img = PoolImage(Geom(n_caches=1, index_dim=pw.Dk, fp8=True), p1 - p0, fill=NAN16)
+    rope_bits = rope.view(torch.int16).numpy().view(np.uint16)
+    key_bits = keys.view(torch.int16).numpy().view(np.uint16)
+    for i in range(T):
+        img.write_row(pt_h, p1, 0, t0 + i, 0, codes[i], rope_bits[i], scale[i])
+    for i in range(j1 - j0):
+        img.write_pkey(pt_h, p1, 0, j0 + i, 0, key_bits[i])
+    got = host(pool)
+    assert np.array_equal(got, img.buf), f"{np.count_nonzero(got != img.buf)} bytes differ"

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import attention_page_table_amd as tf
-from oracle import PoolImage, Geom, topk_blocks
+from oracle import PoolImage, Geom, topk_blocks, quantize_rows
 from oracle import workload as ow
 from oracle.layout import snapshot_copy
 from synth import TAG_LATENT, bf16_values, e4m3_codes, fp8_row_scales, TAG_LAT8, TAG_SCALE8
@@ -348,3 +348,60 @@ def test_fp8_rows(scale):
     lg, nv, blk, out, lse = run_step(wl, plan, P.view(), wl.rows, 512, scale)
     ro, rl = ow.attention(wl, 0, wl.rows, blk, scale)
     check_attention(out, lse, ro, rl, "fp8 tiny")
+
+
+def _bf16_rows(x: np.ndarray):
+    """float32 values rounded to bf16: the device tensor and the same values as float32."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.cuda(), t.to(torch.float32).numpy(), t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_latent_write_quantize():
+    _log("quantizing write: e4m3 codes, row scales, rope and keys against the oracle, byte for byte")
+    wl = tiny(2)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    P = alloc_pool(wl, plan)
+    rng = np.random.default_rng(11)
+    # 384 distinct rows of both streams, the pages' first and last slots among them
+    pos = [(b, t) for b in range(2) for t in (0, 511, 512, 1023, 1536, 2047)]
+    rest = rng.choice(2 * 2048, 384, replace=False)
+    for v in rest:
+        if len(pos) == 384:
+            break
+        bt = (int(v) // 2048, int(v) % 2048)
+        if bt not in pos:
+            pos.append(bt)
+    R = len(pos)
+    x = (rng.standard_normal((R, 512)) / 24.0).astype(np.float32)
+    x[0] = 0.0                                      # an all-zero row
+    x[1] = rng.uniform(-6e-5, 6e-5, 512)            # one large value: the rest code as subnormals
+    x[1, 300] = 3.0
+    x[2, ::2] = -0.0                                # signed zeros
+    x[3] = -np.abs(x[3])
+    x[3, 5] = -1.0                                  # the maximum is negative
+    x[4] = np.float32(1.0) + np.arange(512, dtype=np.float32) / 64.0   # many codes on ties after scaling
+    lat, xf, _ = _bf16_rows(x)
+    rope, _, rope_bits = _bf16_rows(rng.standard_normal((R, 64)) / 24.0)
+    rs = torch.tensor([b for b, _ in pos], dtype=torch.int32, device="cuda")
+    rp = torch.tensor([t for _, t in pos], dtype=torch.int32, device="cuda")
+    keys = [(b, j) for b in range(2) for j in (0, 127, 128, 511)] + [(0, 300), (1, 5)]
+    kv, _, key_bits = _bf16_rows(rng.standard_normal((len(keys), wl.Dk)) / 8.0)
+    ks = torch.tensor([b for b, _ in keys], dtype=torch.int32, device="cuda")
+    kj = torch.tensor([j for _, j in keys], dtype=torch.int32, device="cuda")
+    tf.latent_write_quantize(plan, P.view(), rs, rp, lat, rope, ks, kj, kv)
+    torch.cuda.synchronize()
+    codes, scale = quantize_rows(xf)
+    img = PoolImage(Geom(n_caches=1, index_dim=wl.Dk, fp8=True), wl.n_pages, fill=NAN16)
+    for i, (b, t) in enumerate(pos):
+        img.write_row(wl.pt, wl.pt_stride, b, t, 0, codes[i], rope_bits[i], scale[i])
+    for i, (b, j) in enumerate(keys):
+        img.write_pkey(wl.pt, wl.pt_stride, b, j, 0, key_bits[i])
+    got = host(P.pool)
+    if not np.array_equal(got, img.buf):
+        bad = np.flatnonzero(got != img.buf)
+        raise AssertionError(f"{bad.size} bytes differ, first at {bad[:8]}")
+    assert scale[0] == 0 and np.sum((codes[1] & 0x78) == 0) > 400
+    # the plan's bf16 twin refuses the call
+    plan16 = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    with pytest.raises(tf.TFError):
+        tf.latent_write_quantize(plan16, P.view(), rs, rp, lat, rope)

@@ -1,0 +1,97 @@
+"""The oracle's quantizing-write recipe, pinned without itself: the nearest-code
+search against torch's float8_e4m3fn conversion (a library routine), codes derived
+by hand from the e4m3fn definition, and the recipe's invariants (the row maximum
+codes to +-448, the error bound of a 3-bit mantissa, zero rows)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.fp8 import e4m3_decode, e4m3_encode_nearest, quantize_rows
+
+
+def _torch_codes(q: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.asarray(q, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_nearest_code_against_torch():
+    mags = e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (mags[1:] + mags[:-1]) / 2            # exact ties: every midpoint is an fp32 value
+    rng = np.random.default_rng(3)
+    rand = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1e-2, 20000),
+                           rng.normal(0, 1e-3, 5000)])
+    q = np.concatenate([mags, -mags, mids, -mids, rand, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    np.testing.assert_array_equal(e4m3_encode_nearest(q), _torch_codes(q))
+
+
+def test_codes_by_hand():
+    # e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa bits; subnormals m * 2^-9
+    cases = {
+        1.0: 0x38,        # 0 0111 000
+        -1.0: 0xB8,
+        0.5: 0x30,        # 0 0110 000
+        3.0: 0x44,        # 1.100 x 2^1: 0 1000 100
+        448.0: 0x7E,      # 1.110 x 2^8: 0 1111 110, the largest finite value
+        1.0625: 0x38,     # halfway between 1.0 (m=000) and 1.125 (m=001): the even code
+        1.1875: 0x3A,     # halfway between 1.125 (m=001) and 1.25 (m=010): the even code
+        2.5 / 512: 0x02,  # halfway between subnormals 2 and 3 (x 2^-9): the even code
+        7.5 / 512: 0x08,  # halfway between subnormal 7 and 2^-6 (code 8): the even code
+        2.0 ** -10: 0x00,  # a quarter step below the first subnormal: 0
+        -(2.0 ** -11): 0x80,  # rounds to zero, keeps its sign
+        432.0: 0x7E,      # halfway between 416 (m=101) and 448 (m=110): the even code
+    }
+    q = np.array(list(cases), dtype=np.float32)
+    np.testing.assert_array_equal(e4m3_encode_nearest(q), np.array(list(cases.values()), dtype=np.uint8))
+
+
+def _rows():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 512)) / 24.0).astype(np.float32)
+    x = x.view(np.uint32) & np.uint32(0xFFFF0000)          # bf16 values
+    x = x.view(np.float32)
+    x[1] = 0.0                                              # an all-zero row
+    x[2, :] = rng.uniform(-6e-5, 6e-5, 512).astype(np.float32)
+    x[2, 7] = -3.0                                          # one large value: the rest code as subnormals
+    x[3, ::2] = -0.0                                        # signed zeros in a nonzero row
+    return x
+
+
+def test_recipe_invariants():
+    x = _rows()
+    codes, scale = quantize_rows(x)
+    assert codes.dtype == np.uint8 and codes.shape == x.shape and scale.dtype == np.float32
+    # the zero row
+    assert scale[1] == 0 and np.all(codes[1] == 0)
+    nz = scale > 0
+    # the row maximum codes to +-448 exactly
+    imax = np.argmax(np.abs(x), axis=1)
+    top = codes[np.arange(len(x)), imax]
+    assert np.all((top[nz] & 0x7F) == 0x7E)
+    assert np.all((top[nz] >> 7) == (x[np.arange(len(x)), imax][nz] < 0))
+    # error bound: half a step of a 3-bit mantissa, or half the subnormal step
+    deq = e4m3_decode(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(deq - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
+    assert np.all(err <= bound)
+    # subnormal codes occur in the row with one large value, and signed zeros keep their sign
+    assert np.sum((codes[2] & 0x78) == 0) > 400
+    assert np.all(codes[3, ::2] == 0x80)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_recipe_matches_definition_elementwise(seed):
+    # the same recipe written out one value at a time in float32 and float64 scalars
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((4, 512)) * 0.1).astype(np.float32)
+    codes, scale = quantize_rows(x)
+    mags = e4m3_decode(np.arange(127, dtype=np.uint8))
+    for r in range(4):
+        amax = np.float32(max(abs(float(v)) for v in x[r]))
+        s = np.float32(amax / np.float32(448.0))
+        assert scale[r] == s
+        for i in range(0, 512, 37):
+            qv = float(min(max(np.float32(x[r, i] / s), np.float32(-448.0)), np.float32(448.0)))
+            d = np.abs(mags - abs(qv))
+            best = [c for c in range(127) if d[c] == d.min()]
+            c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            assert codes[r, i] == (c | (0x80 if np.signbit(qv) else 0))
