@@ -333,9 +333,15 @@ __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
   return nv;
 }
 
+// Waves per SIMD a kernel asks the compiler to leave room for: two workgroups of
+// 1,024 threads per CU (8 waves per SIMD, at most 64 VGPRs) where the LDS allows it,
+// so that one workgroup's loads overlap the other's selection.
+template <int E>
+constexpr int kWavesPerSimd = E == 32 ? 8 : 4;
+
 // One workgroup per row.
 template <int E>
-__global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
   const int r = blockIdx.x;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
 // Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row, in
 // index order, padded with key 0 to kp.
 template <int E>
-__global__ __launch_bounds__(kNT) void topk_stage1_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
   const int r = blockIdx.y;
