@@ -479,6 +479,154 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   write_out<HG, F>(a, sh, o, r, split, h0, wave, lane, tid);
 }
 
+// ---- 32 heads, bf16 rows: each wave keeps its own slice of the keys ---------------------
+// With 32 heads per workgroup, wave w's share of S is latent dims [128w, 128w+128) plus
+// rope dims [16w, 16w+16), and its P.V columns are the same latent dims. So a wave
+// gathers its slice of each 32-token tile straight into registers, already in the
+// B-fragment order S wants, and runs its S partial from them; then it stores the
+// slice's 128 latent columns in its own LDS region, for the transposed reads of P.V,
+// and issues the next tile's gather into the same registers. No wave reads another's
+// keys, so a tile needs two barriers (partial S -> softmax, softmax -> P.V) besides the
+// one inside the softmax, and LDS carries each value twice instead of three times.
+constexpr int kVS = 144;   // row stride of a wave's V slice, bf16: 288 bytes, conflict-free
+                           // for the transposed reads (rows 32 banks apart)
+
+struct alignas(16) AttnSharedW {
+  __bf16 vt[4][kTileTok][kVS];   // wave w: tokens x its 128 latent columns
+  float spart[4][32][kSpartStride<32>];
+  __bf16 p_hi[32][kTileTok + 8];
+  __bf16 p_lo[32][kTileTok + 8];
+  float tsc[kTileTok];
+  int32_t tt[kMaxWgTok];
+  float m_run[32], l_run[32], alpha[32];
+  int32_t bad;
+};
+
+__global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
+  typedef Frag<32> F;
+  __shared__ AttnSharedW sh;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+
+  int unit, hg;
+  if (a.ngroups == 1) {
+    unit = blockIdx.x;
+    hg = 0;
+  } else {  // the two head groups of a unit are 8 workgroups apart: same XCD
+    unit = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    hg = (blockIdx.x >> 3) & 1;
+  }
+  if (unit >= a.n_units) return;
+  const int r = unit % a.n_rows, split = unit / a.n_rows;
+  const int h0 = hg * 32;
+  const int b = a.row_stream[r];
+  const int t = a.row_pos[r];
+  const int j0 = split * a.slots_per_split;
+  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
+  const int ntiles = (ntok + kTileTok - 1) / kTileTok;
+
+  if (tid < 32) {
+    sh.m_run[tid] = -__builtin_inff();
+    sh.l_run[tid] = 0.f;
+    sh.tsc[tid] = 1.f;
+  }
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();
+  // ---- token table ----------------------------------------------------------------
+  for (int i = tid; i < ntiles * kTileTok; i += 256) {
+    const int slot = j0 + i / kPoolRatio;
+    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
+    const int s = blk * kPoolRatio + (i & 3);
+    int32_t e = kMasked;
+    if (blk >= 0 && s <= t) {
+      const int page = page_of(a.v, b, s / kPageRows);
+      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
+      if (page < 0) sh.bad = 1;
+    }
+    sh.tt[i] = e;
+  }
+  // ---- query fragments (A: head = lane % 32, this wave's dims) ------------------------
+  bf16x8 aq[F::kSteps];
+  {
+    const int head = h0 + F::a_row(lane);
+    const __bf16* qr = a.q + ((int64_t)r * a.n_heads + head) * kRow;
+#pragma unroll
+    for (int i = 0; i < F::kSteps; ++i)
+      aq[i] = head < a.n_heads ? *(const bf16x8*)(qr + F::ks_dim(wave, i, F::a_half(lane))) : bf16x8{};
+  }
+  F::acc_t o[F::kNT];
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt) o[nt] = F::acc_t{};
+  __syncthreads();
+
+  // this lane's token of each tile and its 9 pieces of 8 dims: B[k][n] of S with
+  // n = the token, k = the wave's dims (8 latent steps, then its rope step)
+  const int tok = F::tok_of_lane(wave, lane), g = F::a_half(lane);
+  bf16x8 kvr[F::kSteps];
+  // a token that is not attended (or whose page the table does not name) gets zeros:
+  // its probability is 0, and 0 x V must not meet unwritten bytes
+  auto gather = [&](int tile) __attribute__((always_inline)) {
+    const int32_t e = sh.tt[tile * kTileTok + tok];
+#pragma unroll
+    for (int i = 0; i < F::kSteps; ++i) kvr[i] = bf16x8{};
+    if (e >= 0) {
+      const int64_t base = row_base(a, e);
+      const char* rowp = a.v.pool + base + (int64_t)(e & 511) * a.lat_row_bytes;
+      const char* ropep = a.v.pool + base + a.off_rope + (int64_t)(e & 511) * (kRope * 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kvr[i] = *(const bf16x8*)(rowp + (wave * 128 + 16 * i + 8 * g) * 2);
+      kvr[8] = *(const bf16x8*)(ropep + (16 * wave + 8 * g) * 2);
+    }
+  };
+  if (ntiles > 0) gather(0);
+  __bf16* vt = &sh.vt[wave][0][0];
+  for (int it = 0; it < ntiles; ++it) {
+    // ---- S partial from the registers ------------------------------------------------
+    F::acc_t accl{}, accr{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) accl = F::mfma(aq[i], kvr[i], accl);
+    accr = F::mfma(aq[8], kvr[8], accr);
+    // ---- the slice's latent columns to this wave's LDS region, then the next gather ----
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(bf16x8*)&vt[tok * kVS + 16 * i + 8 * g] = kvr[i];
+    if (it + 1 < ntiles) gather(it + 1);
+#pragma unroll
+    for (int i = 0; i < F::kAccN; ++i) sh.spart[wave][F::row_of(i, lane)][tok] = accl[i] + accr[i];
+    __syncthreads();
+    softmax_tile<32, F::kParts, false>(sh, sh.tt + it * kTileTok, sh.tsc, a.scale_log2, tid);
+    __syncthreads();
+    // ---- O = alpha O + P V (V from this wave's own slice) --------------------------------
+    {
+      float al[F::kAccN];
+#pragma unroll
+      for (int i = 0; i < F::kAccN; ++i) al[i] = sh.alpha[F::row_of(i, lane)];
+#pragma unroll
+      for (int nt = 0; nt < F::kNT; ++nt)
+#pragma unroll
+        for (int i = 0; i < F::kAccN; ++i) o[nt][i] *= al[i];
+      const int arow = F::a_row(lane), ahalf = F::a_half(lane);
+      const int grp = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int ks = 0; ks < F::kPVsteps; ++ks) {
+        const int tk = ks * F::kPVk + ahalf * 8;
+        const bf16x8 ph = *(const bf16x8*)&sh.p_hi[arow][tk];
+        const bf16x8 pl = *(const bf16x8*)&sh.p_lo[arow][tk];
+#pragma unroll
+        for (int nt = 0; nt < F::kNT; ++nt) {
+          const int k0 = ks * F::kPVk + (grp >> 1) * 8;
+          const int n0 = nt * F::kNTW + (grp & 1) * 16;
+          const bf16x8 vb = bfrag_tr(vt, kVS, k0, n0, j);
+          o[nt] = F::mfma(ph, vb, o[nt]);
+          o[nt] = F::mfma(pl, vb, o[nt]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  write_out<32, F>(a, sh, o, r, split, h0, wave, lane, tid);
+}
+
 // ---- decode: every row of the workgroup in LDS at once ------------------------------------
 // Few rows (decode): a workgroup of 8 waves owns 16 heads and at most 128 tokens of
 // one row; wave w owns tokens 16w .. 16w + 15 from the page lookup to S:
@@ -861,7 +1009,7 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
     else hipLaunchKernelGGL((attn_kernel<16, false>), dim3(p.grid), dim3(256), 0, st, a);
   } else {
     if (fp8) hipLaunchKernelGGL((attn_kernel<32, true>), dim3(p.grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<32, false>), dim3(p.grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(attn_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
   }
   tf_status s = launch_status("tf_sparse_mla_attn");
   if (s != TF_OK || p.nsplit == 1) return s;
