@@ -499,8 +499,60 @@ struct alignas(16) AttnSharedW {
   float tsc[kTileTok];
   int32_t tt[kMaxWgTok];
   float m_run[32], l_run[32], alpha[32];
+  int32_t moved[2];   // by tile parity: some head's max moved in the tile (O needs a rescale)
   int32_t bad;
 };
+
+constexpr float kLazy = 8.f;
+
+__device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t* tt, int it, float scale_log2,
+                                                  int tid) {
+  constexpr int TPH = 8, TPT = kTileTok / TPH;
+  const int h = tid / TPH, p = tid % TPH;
+  typedef float fv_t __attribute__((ext_vector_type(TPT)));
+  typedef int32_t iv_t __attribute__((ext_vector_type(TPT)));
+  typedef __bf16 bv_t __attribute__((ext_vector_type(TPT)));
+  fv_t sv = *(const fv_t*)&sh.spart[0][h][p * TPT];
+#pragma unroll
+  for (int pp = 1; pp < 4; ++pp) sv += *(const fv_t*)&sh.spart[pp][h][p * TPT];
+  const iv_t tv = *(const iv_t*)&tt[p * TPT];
+  float z[TPT];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int e = 0; e < TPT; ++e) {
+    float v = sv[e] * scale_log2;
+    if (tv[e] < 0) v = -__builtin_inff();
+    z[e] = v;
+    tmax = __builtin_fmaxf(tmax, v);
+  }
+  tmax = group_max<TPH>(tmax);
+  const float m_old = sh.m_run[h];
+  const float m_new = (m_old == -__builtin_inff() || tmax > m_old + kLazy) ? tmax : m_old;
+  const float alpha = m_new == m_old ? 1.f : (m_new == -__builtin_inff() ? 1.f : exp2f(m_old - m_new));
+  float lsum = 0.f;
+  bv_t phv, plv;
+#pragma unroll
+  for (int e = 0; e < TPT; ++e) {
+    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
+    lsum += pe;
+    const __bf16 hi = bf16_rne(pe);
+    phv[e] = hi;
+    plv[e] = bf16_rne(pe - bf16_to_f(hi));
+  }
+  *(bv_t*)&sh.p_hi[h][p * TPT] = phv;
+  *(bv_t*)&sh.p_lo[h][p * TPT] = plv;
+  lsum = group_sum<TPH>(lsum);
+  // the other parity's flag was last read in the previous tile's P.V (done: a barrier
+  // since), and is next set in the next tile's softmax (a barrier after this one)
+  if (tid == 0) sh.moved[(it + 1) & 1] = 0;
+  __syncthreads();
+  if (p == 0) {
+    sh.m_run[h] = m_new;
+    sh.l_run[h] = sh.l_run[h] * alpha + lsum;
+    sh.alpha[h] = alpha;
+    if (alpha != 1.f) sh.moved[it & 1] = 1;
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   typedef Frag<32> F;
@@ -531,7 +583,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
     sh.l_run[tid] = 0.f;
     sh.tsc[tid] = 1.f;
   }
-  if (tid == 0) sh.bad = 0;
+  if (tid == 0) {
+    sh.bad = 0;
+    sh.moved[0] = 0;
+    sh.moved[1] = 0;
+  }
   __syncthreads();
   // ---- token table ----------------------------------------------------------------
   for (int i = tid; i < ntiles * kTileTok; i += 256) {
@@ -594,17 +650,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < F::kAccN; ++i) sh.spart[wave][F::row_of(i, lane)][tok] = accl[i] + accr[i];
     __syncthreads();
-    softmax_tile<32, F::kParts, false>(sh, sh.tt + it * kTileTok, sh.tsc, a.scale_log2, tid);
+    softmax_tile_lazy(sh, sh.tt + it * kTileTok, it, a.scale_log2, tid);
     __syncthreads();
-    // ---- O = alpha O + P V (V from this wave's own slice) --------------------------------
     {
-      float al[F::kAccN];
+      if (__builtin_amdgcn_readfirstlane(sh.moved[it & 1]) != 0) {   // some head's max moved
+        float al[F::kAccN];
 #pragma unroll
-      for (int i = 0; i < F::kAccN; ++i) al[i] = sh.alpha[F::row_of(i, lane)];
+        for (int i = 0; i < F::kAccN; ++i) al[i] = sh.alpha[F::row_of(i, lane)];
 #pragma unroll
-      for (int nt = 0; nt < F::kNT; ++nt)
+        for (int nt = 0; nt < F::kNT; ++nt)
 #pragma unroll
-        for (int i = 0; i < F::kAccN; ++i) o[nt][i] *= al[i];
+          for (int i = 0; i < F::kAccN; ++i) o[nt][i] *= al[i];
+      }
       const int arow = F::a_row(lane), ahalf = F::a_half(lane);
       const int grp = lane >> 4, j = lane & 15;
 #pragma unroll
