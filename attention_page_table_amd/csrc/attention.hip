@@ -27,6 +27,9 @@
 //   their heads; the two head groups of one split sit on the same XCD (workgroup
 //   i runs on XCD i mod 8) so the second gather hits L2. Partial (O, max, sum)
 //   go to the workspace and a merge kernel combines them.
+// Three kernels: attn_kernel (the general one above), attn_kernel_w32 (bf16 rows,
+// 32 heads: each wave gathers its own slice of the keys, below) and
+// attn_decode_kernel (few rows: a row's 128 tokens in LDS at once, below).
 #include <math.h>
 
 #include "common.h"
