@@ -405,3 +405,45 @@ def test_latent_write_quantize():
     plan16 = tf.kv_pool_plan(tf.geom(1, wl.Dk))
     with pytest.raises(tf.TFError):
         tf.latent_write_quantize(plan16, P.view(), rs, rp, lat, rope)
+
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_attention_running_max_jumps(tiny_pool, scale):
+    """Queries aimed at one token in each of four later tiles, so that a head's scores
+    on them sit at 5, 11, 14 and 40 (log2 units): the running max of the online
+    softmax jumps mid-row, sometimes by more than 2^8 (O rescaled) and sometimes by
+    less (the tile taken against a max that lags its own). 256 rows, 32 heads, chosen
+    blocks; against the oracle."""
+    _log(f"attention: running-max jumps mid-row, 32 heads, scale {scale:.4f}")
+    from oracle import sparse_mla
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, 32)
+    rows = [(0, t) for t in range(1792, 2048)]
+    R = len(rows)
+    rs, rp, _, _, q = query_inputs(wl, 0, rows)
+    # 64 distinct blocks per row, spread over the visible ones, ascending
+    blk = np.stack([np.round(np.linspace(0, t // 4, wl.k)).astype(np.int32) for _, t in rows])
+    assert all(len(np.unique(b)) == wl.k for b in blk)
+    reader = ow.rows_reader(wl, 0, 0)
+    qf = q.to(torch.float32).cpu().numpy().astype(np.float64)
+    targets_log2 = np.array([5.0, 11.0, 14.0, 40.0])
+    c = targets_log2 / (scale * np.log2(np.e))                 # q . k on each target token
+    for r in range(R):
+        toks = [4 * int(blk[r][j]) for j in (15, 31, 47, 63)]   # tiles 7, 15, 23, 31 of the row
+        lat, rope = reader(toks)
+        kv = np.concatenate([lat, rope], axis=1)               # [4, 576]
+        aim = (c[:, None] * kv / (kv * kv).sum(axis=1, keepdims=True)).sum(axis=0)
+        qf[r, 0::2] += aim                                     # half the heads
+    qd = torch.from_numpy(qf.astype(np.float32)).to(torch.bfloat16).cuda()
+    qexact = qd.to(torch.float32).cpu().numpy().astype(np.float64)
+    blocks = torch.from_numpy(blk).cuda()
+    out = torch.empty((R, 32, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, 32), dtype=torch.float32, device="cuda")
+    tf.sparse_mla_attn(plan, P.view(), rs, rp, qd, scale, blocks, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = sparse_mla(qexact, lambda r, S: reader(S), blk, [t for _, t in rows], scale)
+    # the jumps are there: on aimed heads the last target outscores the first by far
+    lat, rope = reader([4 * int(blk[0][15]), 4 * int(blk[0][63])])
+    z = scale * np.log2(np.e) * (qexact[0] @ np.concatenate([lat, rope], axis=1).T)
+    assert np.all(z[0::2, 1] - z[0::2, 0] > 20)
+    check_attention(host(out), host(lse), ro, rl, "running-max jumps")
