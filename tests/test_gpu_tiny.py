@@ -447,3 +447,18 @@ def test_attention_running_max_jumps(tiny_pool, scale):
     z = scale * np.log2(np.e) * (qexact[0] @ np.concatenate([lat, rope], axis=1).T)
     assert np.all(z[0::2, 1] - z[0::2, 0] > 20)
     check_attention(host(out), host(lse), ro, rl, "running-max jumps")
+
+
+@pytest.mark.parametrize("hq,nrows", [(24, 152), (20, 4)])
+def test_attention_partial_head_group(tiny_pool, hq, nrows):
+    """A head count that fills neither 16 nor 32: the last head group runs with its
+    missing heads masked (never written). 24 heads on many rows (one group of 32),
+    20 heads on decode rows (two groups of 16)."""
+    _log(f"attention: {hq} heads over {nrows} rows (a partial head group)")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, hq)
+    rows = [(0, t) for t in range(1792, 1792 + nrows - 2)] + [(1, 2047), (1, 700)]
+    lg, nv, blk, out, lse = run_step(wl, plan, P.view(), rows, 512, 24.0)
+    assert out.shape == (nrows, hq, 512)
+    ro, rl = ow.attention(wl, 0, rows, blk, 24.0)
+    check_attention(out, lse, ro, rl, f"{hq} heads")
