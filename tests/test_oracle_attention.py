@@ -5,7 +5,7 @@ import math
 
 import numpy as np
 
-from oracle import selected_tokens, sparse_mla_row
+from oracle import dense_mla, dense_mla_row, dense_tokens, selected_tokens, sparse_mla_row
 from oracle.fp8 import e4m3_decode
 
 
@@ -133,3 +133,65 @@ def test_e4m3_decode_all_codes_against_torch():
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], ref[~nan])
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+# ---- dense pass: causal attention over the first n_blocks pooled blocks ----------------
+
+def test_dense_equals_textbook_causal_attention():
+    rng = np.random.default_rng(10)
+    lat = rng.standard_normal((24, 512)) / 24
+    rope = rng.standard_normal((24, 64)) / 24
+    q = rng.standard_normal((2, 576)) / 24
+    for t, n_blocks in ((0, 1), (6, 2), (6, 6), (13, 4), (23, 6), (23, 3), (17, 1)):
+        last = min(t, 4 * n_blocks - 1)           # the extent cuts the causal range
+        for scale in (1 / 24, 24.0):
+            o, l = dense_mla_row(q, rows_from(lat, rope), t, n_blocks, scale)
+            od, ld = dense_textbook(q, lat, rope, last, scale)
+            assert np.allclose(o, od, rtol=1e-12, atol=1e-15), (t, n_blocks, scale)
+            assert np.allclose(l, ld, rtol=1e-12), (t, n_blocks, scale)
+
+
+def test_dense_equals_sparse_with_the_same_blocks_selected():
+    rng = np.random.default_rng(11)
+    lat = rng.standard_normal((40, 512))
+    rope = rng.standard_normal((40, 64))
+    q = rng.standard_normal((3, 576)) / 24
+    for t, n_blocks in ((39, 10), (39, 4), (21, 8), (2, 1)):
+        o, l = dense_mla_row(q, rows_from(lat, rope), t, n_blocks, 2.0)
+        os_, ls = sparse_mla_row(q, rows_from(lat, rope), list(range(n_blocks)), t, 2.0)
+        assert np.allclose(o, os_, rtol=1e-12, atol=1e-14)
+        assert np.allclose(l, ls, rtol=1e-12)
+
+
+def test_dense_closed_forms():
+    rng = np.random.default_rng(12)
+    lat = rng.standard_normal((32, 512))
+    rope = rng.standard_normal((32, 64))
+    q = rng.standard_normal((2, 576))
+    # one visible token: its own row, lse = its score
+    o, l = dense_mla_row(q, rows_from(lat, rope), 0, 5, 0.3)
+    assert np.array_equal(o, np.repeat(lat[:1], 2, axis=0))
+    assert np.allclose(l, 0.3 * (q @ np.concatenate([lat[0], rope[0]])))
+    # zero query: the mean of the visible rows, lse = ln(count)
+    for t, n_blocks, count in ((30, 8, 31), (30, 3, 12)):
+        o, l = dense_mla_row(np.zeros((2, 576)), rows_from(lat, rope), t, n_blocks, 7.0)
+        assert np.allclose(o, lat[:count].mean(axis=0)[None, :], rtol=1e-13)
+        assert np.allclose(l, math.log(count))
+    # a row before the stream's start sees nothing
+    o, l = dense_mla_row(q, rows_from(lat, rope), -1, 4, 1.0)
+    assert not o.any() and np.all(l == -np.inf)
+    assert dense_tokens(9, 2).tolist() == list(range(8))
+    assert dense_tokens(9, 3).tolist() == list(range(10))
+
+
+def test_dense_rows_follow_their_own_streams_and_positions():
+    rng = np.random.default_rng(13)
+    lat = rng.standard_normal((2, 20, 512))
+    rope = rng.standard_normal((2, 20, 64))
+    q = rng.standard_normal((3, 2, 576)) / 24
+    streams, pos = [1, 0, 1], [19, 7, 3]
+    o, l = dense_mla(q, lambda r, S: (lat[streams[r]][S], rope[streams[r]][S]), pos, 5, 1.5)
+    for r in range(3):
+        od, ld = dense_textbook(q[r], lat[streams[r]], rope[streams[r]], pos[r], 1.5)
+        assert np.allclose(o[r], od, rtol=1e-12, atol=1e-15)
+        assert np.allclose(l[r], ld, rtol=1e-12)
