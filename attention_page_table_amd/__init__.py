@@ -62,6 +62,8 @@ SIGNATURES = {
     "tf_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32]),
     "tf_sparse_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
                                     ctypes.c_float, _vp, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_dense_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
+                                   ctypes.c_float, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_attn_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
     "tf_snapshot_copy": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, tf_kv_view, _c_i32, _vp, _vp, _c_i64, _vp]),
     "tf_last_error": (ctypes.c_char_p, []),
@@ -221,6 +223,19 @@ def sparse_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, bloc
     return _run("tf_sparse_mla_attn", (ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
                                        n_heads, float(softmax_scale), _ptr(blocks), k, _ptr(out), _ptr(lse),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+                prepare, keep=(ws,))
+
+
+def dense_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, n_blocks: int, out, lse=None, ws=None,
+                   stream=None, prepare=False):
+    n_rows, n_heads = q.shape[0], q.shape[1]
+    need = attn_workspace_bytes(n_rows, n_heads, n_blocks)
+    if need and ws is None:
+        import torch
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return _run("tf_dense_mla_attn", (ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                      n_heads, float(softmax_scale), int(n_blocks), _ptr(out), _ptr(lse),
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
                 prepare, keep=(ws,))
 
 

@@ -227,3 +227,35 @@ extern "C" tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t
   return launch_attn(p, make_view(p, kv), n_rows, row_stream, row_pos, q, n_heads, softmax_scale, blocks,
                      k, out, lse, ws, ws_bytes, (hipStream_t)stream);
 }
+
+extern "C" tf_status tf_dense_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
+                                       const int32_t* row_stream, const int32_t* row_pos,
+                                       const void* q, int32_t n_heads, float softmax_scale,
+                                       int32_t n_blocks, float* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, kv, "kv")) != TF_OK) return s;
+  if (p->g.rope_dim != kRope)
+    return set_error(TF_E_UNSUPPORTED, "tf_dense_mla_attn: needs the 64-value rope plane");
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_dense_mla_attn: n_rows < 0");
+  if (n_heads < 1 || n_heads > 32)
+    return set_error(TF_E_UNSUPPORTED, "tf_dense_mla_attn: n_heads=%d, built for 1..32", n_heads);
+  if (n_blocks < 1 || n_blocks > 2048)
+    return set_error(TF_E_RANGE,
+                     "tf_dense_mla_attn: n_blocks=%d, need 1..2048 (8,192 tokens); longer contexts go through "
+                     "tf_indexer_logits, tf_topk_blocks and tf_sparse_mla_attn",
+                     n_blocks);
+  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f)
+    return set_error(TF_E_INVAL, "tf_dense_mla_attn: softmax_scale must be > 0");
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !out)
+    return set_error(TF_E_INVAL, "tf_dense_mla_attn: row_stream, row_pos, q and out are required");
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_dense_mla_attn: q must be 16-byte aligned");
+  const size_t need = attn_ws_bytes(n_rows, n_heads, n_blocks);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return set_error(TF_E_INVAL, "tf_dense_mla_attn: workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  return launch_attn(p, make_view(p, kv), n_rows, row_stream, row_pos, q, n_heads, softmax_scale, nullptr,
+                     n_blocks, out, lse, ws, ws_bytes, (hipStream_t)stream);
+}

@@ -27,6 +27,11 @@
 //   their heads; the two head groups of one split sit on the same XCD (workgroup
 //   i runs on XCD i mod 8) so the second gather hits L2. Partial (O, max, sum)
 //   go to the workspace and a merge kernel combines them.
+// The dense pass [#1142, "What stays as it is", and its proposal's kernel list: the
+// page-table kernels read the latent for dense chunks as for the sparse gather]
+// runs the same kernels with no block list: slot j is pooled block j, and a split
+// stops at the row's last visible block. Its split ranges follow from the extent
+// and the row count alone, so a stream's bits never depend on its pages.
 // Three kernels: attn_kernel (the general one above), attn_kernel_w32 (bf16 rows,
 // 32 heads: each wave gathers its own slice of the keys, below) and
 // attn_decode_kernel (few rows: a row's 128 tokens in LDS at once, below).
@@ -60,6 +65,25 @@ struct AttnArgs {
   float* part_o;   // [n_rows][nsplit][32][512]
   float* part_ml;  // [n_rows][nsplit][32][2]  (max in log2 domain, sum)
 };
+
+// A row's block list, or none: the dense pass (blocks == nullptr) names slot j as
+// pooled block j, so the row attends every token s <= t with s < 4 k.
+__device__ __forceinline__ int block_at(const AttnArgs& a, int r, int slot) {
+  return a.blocks ? a.blocks[(int64_t)r * a.k + slot] : slot;
+}
+
+// End of a split's slot range [j0, j1). In the dense pass the slots past the row's
+// last visible block (t / 4) hold masked tokens only and are cut, keeping at least
+// one slot so that the split still writes its (empty) partial for the merge.
+__device__ __forceinline__ int split_end(const AttnArgs& a, int j0, int t) {
+  int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  if (!a.blocks) {
+    const int jv = t >= 0 ? t / kPoolRatio + 1 : 0;
+    const int lim = jv > j0 + 1 ? jv : j0 + 1;
+    j1 = j1 < lim ? j1 : lim;
+  }
+  return j1;
+}
 
 // Row stride of the partial S tiles in floats: 16-byte aligned rows (vector reads in
 // the softmax), and the rows one MFMA store instruction writes land on disjoint LDS
@@ -386,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int b = a.row_stream[r];
   const int t = a.row_pos[r];
   const int j0 = split * a.slots_per_split;
-  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int j1 = split_end(a, j0, t);
   const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
   const int ntiles = (ntok + kTileTok - 1) / kTileTok;
 
@@ -400,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // ---- token table ----------------------------------------------------------------
   for (int i = tid; i < ntiles * kTileTok; i += 256) {
     const int slot = j0 + i / kPoolRatio;
-    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
+    const int blk = slot < j1 ? block_at(a, r, slot) : -1;
     const int s = blk * kPoolRatio + (i & 3);
     int32_t e = kMasked;
     if (blk >= 0 && s <= t) {
@@ -577,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   const int b = a.row_stream[r];
   const int t = a.row_pos[r];
   const int j0 = split * a.slots_per_split;
-  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int j1 = split_end(a, j0, t);
   const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
   const int ntiles = (ntok + kTileTok - 1) / kTileTok;
 
@@ -595,7 +619,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   // ---- token table ----------------------------------------------------------------
   for (int i = tid; i < ntiles * kTileTok; i += 256) {
     const int slot = j0 + i / kPoolRatio;
-    const int blk = slot < j1 ? a.blocks[(int64_t)r * a.k + slot] : -1;
+    const int blk = slot < j1 ? block_at(a, r, slot) : -1;
     const int s = blk * kPoolRatio + (i & 3);
     int32_t e = kMasked;
     if (blk >= 0 && s <= t) {
@@ -740,7 +764,6 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   const int r = unit % a.n_rows, split = unit / a.n_rows;
   const int h0 = hg * 16;
   const int j0 = split * a.slots_per_split;
-  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
 
   // ---- loads with no dependence ------------------------------------------------------
   // Every address is made valid by clamping, so the loads carry no branches and stay
@@ -748,8 +771,9 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   // Lane i < 16 stands for token 16w + i (block slot j0 + 4w + i/4).
   const int b = a.row_stream[r];
   const int t = a.row_pos[r];
+  const int j1 = split_end(a, j0, t);
   const int slot = j0 + 4 * wave + ((lane >> 2) & 3);
-  const int blk_raw = a.blocks[(int64_t)r * a.k + (slot < a.k ? slot : a.k - 1)];
+  const int blk_raw = block_at(a, r, slot < a.k ? slot : a.k - 1);
   {
     // query k-steps w, w + 8 and w + 16 (waves 2.. load k-step w again: same bytes)
     const int hq = h0 + (lane & 15) < a.n_heads ? h0 + (lane & 15) : a.n_heads - 1;   // heads past n_heads are never written
@@ -1071,10 +1095,11 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
     if (fp8) hipLaunchKernelGGL((attn_kernel<32, true>), dim3(p.grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(attn_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
   }
-  tf_status s = launch_status("tf_sparse_mla_attn");
+  const char* name = blocks ? "tf_sparse_mla_attn" : "tf_dense_mla_attn";
+  tf_status s = launch_status(name);
   if (s != TF_OK || p.nsplit == 1) return s;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(n_rows * n_heads), dim3(128), 0, st, a);
-  return launch_status("tf_sparse_mla_attn");
+  return launch_status(name);
 }
 
 }  // namespace tf

@@ -68,6 +68,7 @@ size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k);
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                       int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st);
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
+// blocks == nullptr runs the dense pass over the first k pooled blocks
 tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
                       const int32_t* row_pos, const void* q, int32_t n_heads, float scale,
                       const int32_t* blocks, int32_t k, float* out, float* lse, void* ws,

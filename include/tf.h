@@ -14,7 +14,8 @@
  *                           selected latent rows from the pages (decode rows and
  *                           chunked-prefill rows alike);
  *   plus tf_latent_write_quantize (step 1 for fp8 pages, quantizing bf16 rows on
- *   the device), tf_snapshot_copy (copy only the first `at` rows of a stream) and
+ *   the device), tf_dense_mla_attn (short contexts: attention over every visible
+ *   token, with no indexer or top-k), tf_snapshot_copy (copy only the first `at` rows of a stream) and
  *   the host-side tf_kv_pool_plan / tf_prefill_chunk.
  *
  * Sources (web pages, by title and section):
@@ -217,6 +218,27 @@ tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
                              const void* q, int32_t n_heads, float softmax_scale,
                              const int32_t* blocks, int32_t k, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Dense absorbed-MLA attention [#1142, "What stays as it is", and the kernel
+ * list of its proposal: the page-table kernels read the latent for dense
+ * chunks as well as for the sparse gather]: the short-context pass that skips
+ * the indexer and the top-k. Row r at position t = row_pos[r] attends every
+ * token it sees within the first n_blocks pooled blocks:
+ *   S = {s : s <= t and s < 4 * n_blocks}
+ * and computes out and lse as tf_sparse_mla_attn does over that set (the pages
+ * give no extent; with n_blocks >= t / 4 + 1 for every row it is plain causal
+ * attention). It equals tf_sparse_mla_attn with blocks[r] = 0, 1, ..,
+ * n_blocks - 1 for every row, bit for bit, and a stream's results do not
+ * depend on which pages hold its rows. q, out, lse, the scale and the rows'
+ * formats are as for tf_sparse_mla_attn; 1 <= n_blocks <= 2048 (8,192 tokens;
+ * longer contexts take the sparse path, TF_E_RANGE otherwise). ws: device
+ * workspace of at least tf_attn_workspace_bytes(n_rows, n_heads, n_blocks)
+ * bytes (may be NULL when that is 0). */
+tf_status tf_dense_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
+                            const int32_t* row_stream, const int32_t* row_pos,
+                            const void* q, int32_t n_heads, float softmax_scale,
+                            int32_t n_blocks, float* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
 size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
 
 /* Snapshot [#1142, "Proposal" piece 1]: for each i < n_streams, copy rows

@@ -11,7 +11,7 @@ import numpy as np
 
 from synth import bf16_to_f64
 
-from .attention import sparse_mla
+from .attention import dense_mla, sparse_mla
 from .fp8 import e4m3_decode
 from .indexer import indexer_logits, n_compressed
 from .topk import topk_blocks
@@ -62,6 +62,13 @@ def attention(wl, c: int, rows, blocks: np.ndarray, scale: float):
     readers = {b: rows_reader(wl, c, b) for b in {b for b, _ in rows}}
     return sparse_mla(q, lambda r, S: readers[rows[r][0]](S), blocks,
                       [t for _, t in rows], scale)
+
+
+def dense_attention(wl, c: int, rows, n_blocks: int, scale: float):
+    """The dense pass over the first n_blocks pooled blocks, for the given query rows."""
+    q = bf16_to_f64(wl.q_bits(c, rows))
+    readers = {b: rows_reader(wl, c, b) for b in {b for b, _ in rows}}
+    return dense_mla(q, lambda r, S: readers[rows[r][0]](S), [t for _, t in rows], n_blocks, scale)
 
 
 def step(wl, c: int, rows, ld: int, scale: float):

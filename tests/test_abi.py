@@ -121,6 +121,24 @@ def test_validation_refuses_before_launch():
                                 None) == tf.TF_E_UNSUPPORTED
     assert L.tf_sparse_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, -1.0, fake, 64, fake, None, None, 0,
                                 None) == tf.TF_E_INVAL
+    # the dense pass: extent out of range (longer contexts take the sparse path),
+    # heads, missing query; no rows is a no-op
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, 1.0, 2049, fake, None, None, 0,
+                               None) == tf.TF_E_RANGE
+    assert "tf_sparse_mla_attn" in L.tf_last_error().decode()
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, 1.0, 0, fake, None, None, 0,
+                               None) == tf.TF_E_RANGE
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 40, 1.0, 64, fake, None, None, 0,
+                               None) == tf.TF_E_UNSUPPORTED
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, None, 32, 1.0, 64, fake, None, None, 0,
+                               None) == tf.TF_E_INVAL
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, 0.0, 64, fake, None, None, 0,
+                               None) == tf.TF_E_INVAL
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 8, fake, fake, fake, 32, 1.0, 1024, fake, None, None, 0,
+                               None) == tf.TF_E_INVAL
+    assert "workspace" in L.tf_last_error().decode()
+    assert L.tf_dense_mla_attn(ctypes.byref(p), v, 0, None, None, None, 32, 1.0, 64, None, None, None, 0,
+                               None) == tf.TF_OK
     # null plan, null pool
     assert L.tf_latent_write(None, v, 1, fake, fake, fake, None, fake, 0, None, None, None, None) == tf.TF_E_INVAL
     nv = tf.tf_kv_view(None, None, 4, 4, 16, 0)

@@ -230,3 +230,35 @@ def test_quantizing_write_chunk_full():
         img.write_pkey(pt_h, p1, 0, j0 + i, 0, key_bits[i])
     got = host(pool)
     assert np.array_equal(got, img.buf), f"{np.count_nonzero(got != img.buf)} bytes differ"
+
+
+def test_dense_chunk_full():
+    """The dense pass over a 2,048-row chunk at L = 4,096 (rows [2,048, 4,096), each
+    row's whole causal range: n_blocks = 1,024), in the launch configuration the bench
+    times: sampled rows against the oracle at both scales, and every row equal, bit
+    for bit, to the sparse pass with blocks 0 .. 1,023 selected."""
+    wl = prefill_chunk(0, L=4096, T=2048, slack_pages=4)
+    _log("dense chunk: populating")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows, nb = wl.rows, 1024
+    R = len(rows)
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    blocks = torch.arange(nb, dtype=torch.int32, device="cuda").repeat(R, 1).contiguous()
+    rng = np.random.default_rng(8)
+    sample = sorted(set([0, 1, 1023, 2046, 2047] + rng.choice(2048, 8, replace=False).tolist()))
+    srows = [rows[i] for i in sample]
+    for sc in SCALES:
+        out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+        tf.dense_mla_attn(plan, P.view(), rs, rp, q, sc, nb, out, lse)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        tf.sparse_mla_attn(plan, P.view(), rs, rp, q, sc, blocks, out2, lse2)
+        torch.cuda.synchronize()
+        _log(f"dense chunk: dense == sparse over every block, scale {sc:.4f}")
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
+        _log(f"dense chunk: oracle on {len(sample)} sampled rows")
+        ro, rl = ow.dense_attention(wl, 0, srows, nb, sc)
+        check_attention(host(out)[sample], host(lse)[sample], ro, rl, f"dense chunk scale {sc}")

@@ -462,3 +462,99 @@ def test_attention_partial_head_group(tiny_pool, hq, nrows):
     assert out.shape == (nrows, hq, 512)
     ro, rl = ow.attention(wl, 0, rows, blk, 24.0)
     check_attention(out, lse, ro, rl, f"{hq} heads")
+
+
+# ---- the dense pass (no indexer, no top-k) -------------------------------------------
+
+def run_dense(wl, plan, view, rows, n_blocks, scale):
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    R = len(rows)
+    out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+    tf.dense_mla_attn(plan, view, rs, rp, q, scale, n_blocks, out, lse)
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+# decode rows (few rows: the 128-token kernel, splits past a row's position cut to
+# one masked slot), and a chunk with early positions (many rows: the 32-head sliced
+# kernel or the 16-head kernel)
+DENSE_ROWS = {
+    "decode": [(0, 2047), (1, 2047), (1, 0), (0, 130), (1, 1029)],
+    "chunk": [(0, t) for t in range(1792, 2048)] + [(1, t) for t in (0, 1, 2, 3, 4, 63, 511, 512, 1500)],
+}
+
+
+@pytest.mark.parametrize("hq", [8, 32])
+@pytest.mark.parametrize("kind", ["decode", "chunk"])
+@pytest.mark.parametrize("n_blocks", [512, 300, 1024])
+def test_dense_against_oracle(tiny_pool, hq, kind, n_blocks):
+    """Every visible token within the first n_blocks blocks: 512 covers each row's
+    causal range exactly, 300 cuts the later rows at token 1,199, 1024 runs past the
+    streams (two splits for the chunk, the second all masked)."""
+    _log(f"dense pass: {kind} rows, {hq} heads, n_blocks {n_blocks} (tiny)")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, hq)
+    rows = DENSE_ROWS[kind]
+    scale = 24.0 if n_blocks != 300 else SCALES[0]
+    out, lse = run_dense(wl, plan, P.view(), rows, n_blocks, scale)
+    ro, rl = ow.dense_attention(wl, 0, rows, n_blocks, scale)
+    check_attention(out, lse, ro, rl, f"dense {kind}")
+
+
+@pytest.mark.parametrize("kind", ["decode", "chunk"])
+@pytest.mark.parametrize("n_blocks", [512, 200])
+def test_dense_equals_sparse_on_every_block_bitwise(tiny_pool, kind, n_blocks):
+    """The dense pass is the sparse pass with blocks 0 .. n_blocks - 1 selected: same
+    bits (the slots it cuts hold masked tokens only)."""
+    _log(f"dense == sparse over blocks 0..{n_blocks - 1}, bit for bit ({kind})")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, 32)
+    rows = DENSE_ROWS[kind]
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    R = len(rows)
+    blocks = torch.arange(n_blocks, dtype=torch.int32, device="cuda").repeat(R, 1).contiguous()
+    outs = []
+    for dense in (True, False):
+        out = torch.full((R, 32, 512), 7.0, dtype=torch.float32, device="cuda")
+        lse = torch.full((R, 32), 7.0, dtype=torch.float32, device="cuda")
+        if dense:
+            tf.dense_mla_attn(plan, P.view(), rs, rp, q, 24.0, n_blocks, out, lse)
+        else:
+            tf.sparse_mla_attn(plan, P.view(), rs, rp, q, 24.0, blocks, out, lse)
+        torch.cuda.synchronize()
+        outs.append((host(out), host(lse)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_dense_bits_do_not_depend_on_pages(tiny_pool):
+    """The same streams in a contiguous window (null table) give the same bits."""
+    _log("dense pass: paged == contiguous window, bit for bit (tiny)")
+    wl, plan, P = tiny_pool
+    wl = _with_heads(wl, 32)
+    contig = torch.empty(8 * plan.page_bytes, dtype=torch.uint8, device="cuda")
+    contig.view(torch.int16).fill_(NAN16)
+    s = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    tf.snapshot_copy(plan, P.view(), tf.view(contig, None, 4, 8), s, s, 2048)
+    for kind in ("decode", "chunk"):
+        a = run_dense(wl, plan, P.view(), DENSE_ROWS[kind], 512, 24.0)
+        b = run_dense(wl, plan, tf.view(contig, None, 4, 8), DENSE_ROWS[kind], 512, 24.0)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("hq", [8, 32])
+def test_dense_fp8_rows(hq):
+    _log(f"dense pass over fp8 rows, {hq} heads (tiny)")
+    wl = tiny(1)
+    wl.fp8 = True
+    wl = _with_heads(wl, hq)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    torch.cuda.synchronize()
+    rows = DENSE_ROWS["decode"] + DENSE_ROWS["chunk"][::4]
+    out, lse = run_dense(wl, plan, P.view(), rows, 512, 24.0)
+    ro, rl = ow.dense_attention(wl, 0, rows, 512, 24.0)
+    check_attention(out, lse, ro, rl, "dense fp8")
