@@ -34,7 +34,9 @@
 // and the row count alone, so a stream's bits never depend on its pages.
 // Three kernels: attn_kernel (the general one above), attn_kernel_w32 (bf16 rows,
 // 32 heads: each wave gathers its own slice of the keys, below) and
-// attn_decode_kernel (few rows: a row's 128 tokens in LDS at once, below).
+// attn_decode_kernel (few rows: a row's 128 tokens in LDS at once, below). The
+// 32-head one has a dense instance of its own, attn_dense_kernel_w32, that reads no
+// block list; the others test for the list at run time.
 #include <math.h>
 
 #include "common.h"
@@ -75,14 +77,15 @@ __device__ __forceinline__ int block_at(const AttnArgs& a, int r, int slot) {
 // End of a split's slot range [j0, j1). In the dense pass the slots past the row's
 // last visible block (t / 4) hold masked tokens only and are cut, keeping at least
 // one slot so that the split still writes its (empty) partial for the merge.
+__device__ __forceinline__ int dense_split_end(const AttnArgs& a, int j0, int t) {
+  const int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
+  const int jv = t >= 0 ? t / kPoolRatio + 1 : 0;
+  const int lim = jv > j0 + 1 ? jv : j0 + 1;
+  return j1 < lim ? j1 : lim;
+}
+
 __device__ __forceinline__ int split_end(const AttnArgs& a, int j0, int t) {
-  int j1 = j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k;
-  if (!a.blocks) {
-    const int jv = t >= 0 ? t / kPoolRatio + 1 : 0;
-    const int lim = jv > j0 + 1 ? jv : j0 + 1;
-    j1 = j1 < lim ? j1 : lim;
-  }
-  return j1;
+  return a.blocks ? (j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k) : dense_split_end(a, j0, t);
 }
 
 // Row stride of the partial S tiles in floats: 16-byte aligned rows (vector reads in
@@ -581,9 +584,9 @@ __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
+template <bool DENSE>
+__device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh) {
   typedef Frag<32> F;
-  __shared__ AttnSharedW sh;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   const int b = a.row_stream[r];
   const int t = a.row_pos[r];
   const int j0 = split * a.slots_per_split;
-  const int j1 = split_end(a, j0, t);
+  const int j1 = DENSE ? dense_split_end(a, j0, t) : split_end(a, j0, t);
   const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
   const int ntiles = (ntok + kTileTok - 1) / kTileTok;
 
@@ -619,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   // ---- token table ----------------------------------------------------------------
   for (int i = tid; i < ntiles * kTileTok; i += 256) {
     const int slot = j0 + i / kPoolRatio;
-    const int blk = slot < j1 ? block_at(a, r, slot) : -1;
+    const int blk = slot < j1 ? (DENSE ? slot : block_at(a, r, slot)) : -1;
     const int s = blk * kPoolRatio + (i & 3);
     int32_t e = kMasked;
     if (blk >= 0 && s <= t) {
@@ -709,6 +712,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   }
   __syncthreads();
   write_out<32, F>(a, sh, o, r, split, h0, wave, lane, tid);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
+  __shared__ AttnSharedW sh;
+  attn_w32_body<false>(a, sh);
+}
+
+// The dense pass's instance: no block list to read (slot j is block j).
+__global__ __launch_bounds__(256, 2) void attn_dense_kernel_w32(AttnArgs a) {
+  __shared__ AttnSharedW sh;
+  attn_w32_body<true>(a, sh);
 }
 
 // ---- decode: every row of the workgroup in LDS at once ------------------------------------
@@ -1093,7 +1107,8 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
     else hipLaunchKernelGGL((attn_kernel<16, false>), dim3(p.grid), dim3(256), 0, st, a);
   } else {
     if (fp8) hipLaunchKernelGGL((attn_kernel<32, true>), dim3(p.grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(attn_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
+    else if (blocks) hipLaunchKernelGGL(attn_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(attn_dense_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
   }
   const char* name = blocks ? "tf_sparse_mla_attn" : "tf_dense_mla_attn";
   tf_status s = launch_status(name);

@@ -20,7 +20,8 @@ Reported:
   its average duration from HIP events on the launch stream), with the HBM
   traffic the rocprofv3 counters measured for it when they match the source;
 * the prefill-chunk indexer (T = 2,048 rows against 25,000 pooled keys) against
-  the bf16 MFMA roofline;
+  the bf16 MFMA roofline, and the whole prefill-chunk step call by call;
+* the dense pass (no indexer or top-k) over a 2,048-row chunk at L = 4,096;
 * the oracle timed on the host cores on a bounded sample of the same step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
@@ -62,6 +63,7 @@ ENTRIES = {
     "topk_prefill": (("tf::topk_row_kernel",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
     "attention_prefill": (("tf::attn_kernel",), "attention.hip"),
+    "attention_dense": (("tf::attn_dense_kernel_w32",), "attention.hip"),
 }
 TRAFFIC_FILE = "traffic_bench_decode_8x131072_prefill_indexer_2048_at_100000.json"
 CAL_KERNEL = "neg_kernel"      # torch.neg over CAL_BYTES of float32: a plain streaming copy
@@ -137,6 +139,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=6, help="pool copies rotated between steps")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed passes of the whole prefill-chunk step")
+    ap.add_argument("--dense-reps", type=int, default=10, help="timed calls of the dense pass")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket the dominant call with events on every n-th timed step")
     ap.add_argument("--no-cpu", action="store_true")
@@ -287,7 +290,7 @@ def main():
                 "events_every": every}
 
     # ------------------------------------------------------------------ prefill indexer
-    prefill = prefill_step = None
+    prefill = prefill_step = dense = None
     if not args.no_prefill:
         del launches, views, pools, P0
         torch.cuda.empty_cache()
@@ -322,6 +325,8 @@ def main():
                                 "traffic": load_traffic("indexer_prefill")}}
         prefill_step = bench_prefill_step(tf, pw, pplan, PP, prs, prp, piq, pww, plog, pnv, args.prefill_reps)
         del PP, plog
+        torch.cuda.empty_cache()
+        dense = bench_dense(tf, args.dense_reps)
 
     # ------------------------------------------------------------------ oracle on the host
     cpu = None
@@ -343,6 +348,7 @@ def main():
         "kernels": kern,
         "prefill_indexer": prefill,
         "prefill_step": prefill_step,
+        "dense_pass": dense,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }
@@ -465,6 +471,50 @@ def bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm):
             "roofline": hbm(nbytes, us)}
 
 
+def bench_dense(tf, reps):
+    """The dense pass (tf_dense_mla_attn, no indexer or top-k) over a 2,048-row chunk at
+    L = 4,096: rows [2,048, 4,096) of one stream, each over its whole causal range
+    (n_blocks = 1,024), 32 heads. Timed with fence-free events over `reps` back-to-back
+    calls; the pool is resident. MFMA work: 4 x 32 x 576 flop per (row, attended token),
+    the scores and the value product; each attended token is a 1,152-byte row gathered."""
+    import numpy as np
+    import torch
+    from synth.configs import prefill_chunk
+    from synth.device import alloc_pool, populate, query_inputs
+    dw = prefill_chunk(0, L=4096, T=2048, slack_pages=4)
+    plan = tf.kv_pool_plan(tf.geom(1, dw.Dk))
+    log(f"setup: dense pass over {dw.name}")
+    P = alloc_pool(dw, plan)
+    populate(P)
+    rs, rp, _, _, q = query_inputs(dw, 0, dw.rows)
+    R = len(dw.rows)
+    nb = dw.rows[-1][1] // 4 + 1
+    out = torch.empty((R, dw.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, dw.Hq), dtype=torch.float32, device="cuda")
+    f = tf.dense_mla_attn(plan, P.view(), rs, rp, q, 1.0 / math.sqrt(576.0), nb, out, lse, prepare=True)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    ev = [TimingEvent() for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        f()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+    tokens = sum(min(t + 1, 4 * nb) for _, t in dw.rows)
+    flop = tokens * 4 * dw.Hq * 576
+    a = flop / (us * 1e-6) / 1e12
+    del P
+    return {"call": "tf_dense_mla_attn", "launches": list(ENTRIES["attention_dense"][0]) + ["tf::attn_merge_kernel"],
+            "workload": f"dense_{R}_at_{dw.lengths[0]}", "rows": R, "n_blocks": nb, "attn_heads": dw.Hq,
+            "us": round(us, 2), "reps": reps, "attended_tokens": tokens, "flop": flop,
+            "gathered_bytes": tokens * ROW_BYTES,
+            "gathered_GBps": round(tokens * ROW_BYTES / (us * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic("attention_dense")}}
+
+
 def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
     """The oracle (fp64 numpy) on the same decode step: logits over every pooled
     key, exact top-k, attention over the selected rows, repeated for about
@@ -580,6 +630,8 @@ def summarize_trace(db, label, command, bench_json=None):
         for call, e in (("topk", "topk_prefill"), ("attention", "attention_prefill")):
             if b.get("prefill_step"):
                 ev[e] = b["prefill_step"]["calls"][call]["us"]
+        if b.get("dense_pass"):
+            ev["attention_dense"] = b["dense_pass"]["us"]
         for e, us in ev.items():
             k = sum(a for _, _, a in per_entry.get(e, []))
             lines.append(f"{e:16s} events {us:9.2f} us   kernels {k:9.2f} us   ratio {us / k if k else 0:.3f}")

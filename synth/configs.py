@@ -174,7 +174,7 @@ def prefill_chunk(seed: int = 0, L: int = 100000, T: int = 2048, slack_pages: in
     n = _pages(L)
     pt = _shuffled_tables(rng, n + slack_pages, [n], n)
     rows = [(0, t) for t in range(L - T, L)]
-    return Workload("prefill_2048_at_100000", seed, 1, 1, [L], H=16, Dk=128, Hq=32, k=512,
+    return Workload(f"prefill_{T}_at_{L}", seed, 1, 1, [L], H=16, Dk=128, Hq=32, k=512,
                     n_pages=n + slack_pages, pt=pt, w_d=16.0, rows=rows,
                     description=f"one stream, chunk rows [{L - T}, {L}), keys {L // 4}")
 
