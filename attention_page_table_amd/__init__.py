@@ -62,6 +62,9 @@ SIGNATURES = {
     "tf_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32]),
     "tf_sparse_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
                                     ctypes.c_float, _vp, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_indexer_topk": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32, _c_i64,
+                                 _c_i32, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_indexer_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
     "tf_dense_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
                                    ctypes.c_float, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_attn_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
@@ -206,6 +209,22 @@ def topk_blocks(logits, n_valid, k: int, blocks, ws=None, stream=None, prepare=F
         ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
     return _run("tf_topk_blocks", (_ptr(logits), ld, n_rows, _ptr(n_valid), k, _ptr(blocks), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)), prepare, keep=(ws,))
+
+
+def indexer_topk_workspace_bytes(n_rows: int, ld: int, k: int, key_block: int) -> int:
+    return int(lib().tf_indexer_topk_workspace_bytes(n_rows, ld, k, key_block))
+
+
+def indexer_topk(plan, keys, row_stream, row_pos, q, w, ld: int, k: int, key_block: int, blocks, n_valid=None,
+                 ws=None, stream=None, prepare=False):
+    n_rows, H = w.shape
+    if ws is None:
+        import torch
+        ws = torch.empty(max(1, indexer_topk_workspace_bytes(n_rows, ld, k, key_block)), dtype=torch.uint8,
+                         device=w.device)
+    return _run("tf_indexer_topk", (ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                    _ptr(w), H, int(ld), int(k), int(key_block), _ptr(blocks), _ptr(n_valid),
+                                    _ptr(ws), ws.numel(), _stream(stream)), prepare, keep=(ws,))
 
 
 def attn_workspace_bytes(n_rows: int, n_heads: int, k: int) -> int:

@@ -169,7 +169,7 @@ extern "C" tf_status tf_indexer_logits(const tf_plan* p, tf_kv_view keys, int32_
     return set_error(TF_E_INVAL, "tf_indexer_logits: row_stream, row_pos, q, w and logits are required");
   if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_indexer_logits: q must be 16-byte aligned");
   return launch_indexer(p, make_view(p, keys), n_rows, row_stream, row_pos, q, w, n_heads, logits, ld,
-                        n_valid, (hipStream_t)stream);
+                        n_valid, (hipStream_t)stream, 0, ld, ld);
 }
 
 extern "C" size_t tf_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k) {
@@ -193,6 +193,64 @@ extern "C" tf_status tf_topk_blocks(const float* logits, int64_t ld, int32_t n_r
   if (need > 0 && (!ws || ws_bytes < need))
     return set_error(TF_E_INVAL, "tf_topk_blocks: workspace of %zu bytes needed, got %zu", need, ws_bytes);
   return launch_topk(logits, ld, n_rows, n_valid, k, blocks, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// Key-blocked workspace: one block of logits, the blocks' candidates, then n_c.
+static size_t idxtopk_ws(int32_t n_rows, int64_t ld, int32_t k, int32_t key_block, int64_t* nb_out) {
+  const int64_t nb = (ld + key_block - 1) / key_block;
+  if (nb_out) *nb_out = nb;
+  return (size_t)n_rows * key_block * 4 + topk_cand_bytes(n_rows, (int32_t)nb, k) + ((size_t)n_rows * 4 + 15) / 16 * 16;
+}
+
+extern "C" size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t key_block) {
+  if (n_rows <= 0 || ld <= 0 || k <= 0 || key_block <= 0) return 0;
+  return idxtopk_ws(n_rows, ld, k, key_block, nullptr);
+}
+
+extern "C" tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
+                                     const int32_t* row_stream, const int32_t* row_pos, const void* q,
+                                     const float* w, int32_t n_heads, int64_t ld, int32_t k,
+                                     int32_t key_block, int32_t* blocks, int32_t* n_valid, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, keys, "keys")) != TF_OK) return s;
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_indexer_topk: n_rows < 0");
+  if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_indexer_topk: n_rows=%d, at most 65535 a call", n_rows);
+  if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_indexer_topk: ld=%lld", (long long)ld);
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_indexer_topk: k=%d, need 1..2048", k);
+  if (key_block < kKeysPerPage || key_block > 32768 || key_block % kKeysPerPage != 0)
+    return set_error(TF_E_INVAL, "tf_indexer_topk: key_block=%d, need a multiple of 128 in 128..32768", key_block);
+  if (n_heads != 4 && n_heads != 8 && n_heads != 16)
+    return set_error(TF_E_UNSUPPORTED, "tf_indexer_topk: n_heads=%d, built for 4, 8 or 16", n_heads);
+  int64_t nb = 0;
+  const size_t need = idxtopk_ws(n_rows, ld, k, key_block, &nb);
+  if (nb * ((k + 3) / 4 * 4) > 32768)
+    return set_error(TF_E_RANGE,
+                     "tf_indexer_topk: %lld key blocks x %d candidates exceed the merge's 32,768; raise key_block",
+                     (long long)nb, k);
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !w || !blocks)
+    return set_error(TF_E_INVAL, "tf_indexer_topk: row_stream, row_pos, q, w and blocks are required");
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_indexer_topk: q must be 16-byte aligned");
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return set_error(TF_E_INVAL, "tf_indexer_topk: a 16-byte aligned workspace of %zu bytes is needed, got %zu",
+                     need, ws_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  const DevView v = make_view(p, keys);
+  float* lbuf = (float*)ws;
+  char* cand = (char*)ws + (size_t)n_rows * key_block * 4;
+  int32_t* nv = n_valid ? n_valid : (int32_t*)(cand + topk_cand_bytes(n_rows, (int32_t)nb, k));
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t k0 = b * key_block, k1 = k0 + key_block < ld ? k0 + key_block : ld;
+    if ((s = launch_indexer(p, v, n_rows, row_stream, row_pos, q, w, n_heads, lbuf, key_block, b == 0 ? nv : nullptr,
+                            st, k0, k1, ld)) != TF_OK)
+      return s;
+    if ((s = launch_topk_block(lbuf, key_block, (int32_t)b, (int32_t)nb, ld, n_rows, nv, k, cand, st)) != TF_OK)
+      return s;
+  }
+  return launch_topk_merge(key_block, (int32_t)nb, ld, n_rows, nv, k, blocks, cand, st);
 }
 
 extern "C" size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {

@@ -60,13 +60,21 @@ tf_status launch_latent_write(const tf_plan* p, const DevView& v, int32_t n_rows
 tf_status launch_snapshot(const tf_plan* p, const tf_kv_view& src, const tf_kv_view& dst,
                           int32_t n_streams, const int32_t* src_stream, const int32_t* dst_stream,
                           int64_t at, hipStream_t st);
+// Scores keys [key0, kend) into logits[row * ld + (key - key0)]; n_c is clipped to
+// ncap (the whole call: key0 = 0, kend = ncap = ld).
 tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows,
                          const int32_t* row_stream, const int32_t* row_pos, const void* q,
                          const float* w, int32_t n_heads, float* logits, int64_t ld,
-                         int32_t* n_valid, hipStream_t st);
+                         int32_t* n_valid, hipStream_t st, int64_t key0, int64_t kend, int64_t ncap);
 size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k);
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                       int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st);
+// key-blocked top-k: stage 1 of key block b (logits_blk is [n_rows][B]), then the merge
+size_t topk_cand_bytes(int32_t n_rows, int32_t nb, int32_t k);
+tf_status launch_topk_block(const float* logits_blk, int32_t B, int32_t b, int32_t nb, int64_t ncap,
+                            int32_t n_rows, const int32_t* n_valid, int32_t k, void* cand, hipStream_t st);
+tf_status launch_topk_merge(int32_t B, int32_t nb, int64_t ncap, int32_t n_rows, const int32_t* n_valid,
+                            int32_t k, int32_t* blocks, void* cand, hipStream_t st);
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
 // blocks == nullptr runs the dense pass over the first k pooled blocks
 tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,

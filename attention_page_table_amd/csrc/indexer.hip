@@ -36,8 +36,12 @@ struct IdxArgs {
   const int32_t* row_pos;
   const __bf16* q;
   const float* w;
-  float* logits;
-  int64_t ld;
+  float* logits;   // logit of (row, key) at logits[row * ldo + key]: the caller's buffer
+                   // shifted back by key0 elements (keys below key0 are never written)
+  int64_t ldo;     // row stride of the logits
+  int64_t key0;    // keys [key0, kend) are scored (key0 a multiple of 128)
+  int64_t kend;
+  int64_t ncap;    // n_c is clipped here (the full key count; n_valid receives it)
   int32_t* n_valid;
   int32_t keys_per_wg;   // multiple of 128
   int32_t n_kgroups;
@@ -66,7 +70,7 @@ __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
   const int pos = a.row_pos[row];
   if (pos < 0) return 0;
   const int64_t nc = (int64_t)pos / kPoolRatio + 1;
-  return (int)(nc < a.ld ? nc : a.ld);
+  return (int)(nc < a.ncap ? nc : a.ncap);
 }
 
 // ---- per-row path: one wave streams one row over keys [kb, ke) ---------------------------
@@ -80,7 +84,7 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
   const int b = a.row_stream[row];
   const int nc = nc_of(a, row);
   const float ninf = -__builtin_inff();
-  float* out = a.logits + (int64_t)row * a.ld;
+  float* out = a.logits + (int64_t)row * a.ldo;
   bf16x8 aq[KS];
   {
     const int m = n;
@@ -153,8 +157,8 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
   if (kg >= a.n_kgroups) return;
   const int row = rg * 4 + wave;
   if (row >= a.n_rows) return;
-  const int64_t kb = (int64_t)kg * a.keys_per_wg;
-  const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  const int64_t kb = a.key0 + (int64_t)kg * a.keys_per_wg;
+  const int64_t ke = kb + a.keys_per_wg < a.kend ? kb + a.keys_per_wg : a.kend;
   // one-page ranges over a table of at most 64 streams: read every stream's entry for
   // the page now, beside the row's own stream id
   const bool spec = a.keys_per_wg == kKeysPerPage && a.v.n_streams <= 64;
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int row_base = blockIdx.y * ROWS;
-  const int64_t kb = (int64_t)blockIdx.x * a.keys_per_wg;
-  const int64_t ke = kb + a.keys_per_wg < a.ld ? kb + a.keys_per_wg : a.ld;
+  const int64_t kb = a.key0 + (int64_t)blockIdx.x * a.keys_per_wg;
+  const int64_t ke = kb + a.keys_per_wg < a.kend ? kb + a.keys_per_wg : a.kend;
   const int wave_row0 = row_base + wave * (MT * RPT);
 
   if (blockIdx.x == 0 && a.n_valid && tid < ROWS && row_base + tid < a.n_rows)
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < RH; ++r) optr[t][r] = a.logits + (int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ld + n;
+    for (int r = 0; r < RH; ++r) optr[t][r] = a.logits + (int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ldo + n;
   __syncthreads();
 
   // global -> LDS loads of one 128-key chunk (one page, since kb is a multiple of
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   // keys past every row's compressed length
   const int64_t kf = kend > kb ? kend : kb;
   for (int rr = wave; rr < ROWS; rr += 4)
-    for (int64_t key = kf + lane; key < ke; key += 64) a.logits[(int64_t)(row_base + rr) * a.ld + key] = ninf;
+    for (int64_t key = kf + lane; key < ke; key += 64) a.logits[(int64_t)(row_base + rr) * a.ldo + key] = ninf;
 }
 
 template <int H, int D>
@@ -426,12 +430,13 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
     constexpr int ROWS = 4 * MT * RPT;
     const int64_t rgroups = (n_rows + ROWS - 1) / ROWS;
     // about 1,024 workgroups (four per CU), each over a multiple of 128 keys (at most 4,096)
-    int64_t kpw = (a.ld * rgroups + 1023) / 1024;
+    const int64_t nk = a.kend - a.key0;
+    int64_t kpw = (nk * rgroups + 1023) / 1024;
     kpw = (kpw + 127) / 128 * 128;
     if (kpw < 128) kpw = 128;
     if (kpw > 4096) kpw = 4096;
     a.keys_per_wg = (int32_t)kpw;
-    const int64_t kgroups = (a.ld + kpw - 1) / kpw;
+    const int64_t kgroups = (nk + kpw - 1) / kpw;
     a.n_kgroups = (int32_t)kgroups;
     if (rgroups > 65535) return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows for one launch");
     hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT>), dim3((unsigned)kgroups, (unsigned)rgroups), dim3(256), 0,
@@ -440,12 +445,13 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
     // each wave one row; about 2,048 waves in all (eight per CU keep more key loads in
     // flight than four); a wave's range spans at most 64 pages
     const int n_rg = (n_rows + 3) / 4;
-    int64_t kpw = (a.ld * n_rows + 2047) / 2048;
+    const int64_t nk = a.kend - a.key0;
+    int64_t kpw = (nk * n_rows + 2047) / 2048;
     kpw = (kpw + 127) / 128 * 128;
     if (kpw < 128) kpw = 128;
     if (kpw > 64 * 128) kpw = 64 * 128;
     a.keys_per_wg = (int32_t)kpw;
-    const int64_t kgroups = (a.ld + kpw - 1) / kpw;
+    const int64_t kgroups = (nk + kpw - 1) / kpw;
     a.n_kgroups = (int32_t)kgroups;
     const int64_t grid = ((kgroups + 7) / 8) * 8 * n_rg;
     if (grid > 0x7fffffffLL) return set_error(TF_E_RANGE, "tf_indexer_logits: too many keys for one launch");
@@ -456,7 +462,8 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
 
 tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
                          const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
-                         float* logits, int64_t ld, int32_t* n_valid, hipStream_t st) {
+                         float* logits, int64_t ld, int32_t* n_valid, hipStream_t st, int64_t key0,
+                         int64_t kend, int64_t ncap) {
   IdxArgs a;
   a.v = v;
   a.off_pkey = p->off_pkey;
@@ -466,8 +473,11 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, con
   a.row_pos = row_pos;
   a.q = (const __bf16*)q;
   a.w = w;
-  a.logits = logits;
-  a.ld = ld;
+  a.logits = (float*)((uintptr_t)logits - (uintptr_t)key0 * sizeof(float));   // never read below logits
+  a.ldo = ld;
+  a.key0 = key0;
+  a.kend = kend;
+  a.ncap = ncap;
   a.n_valid = n_valid;
   a.keys_per_wg = 128;
   a.n_kgroups = 1;

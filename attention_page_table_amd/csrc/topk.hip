@@ -313,7 +313,8 @@ __device__ void select_topk(const uint32_t (&key)[E], int k, SelShared& sh, Cand
 
 struct TopkArgs {
   const float* logits;
-  int64_t ld;
+  int64_t ld;         // row stride of the logits
+  int64_t ncap;       // n_valid is clipped here (the row's key count)
   int32_t n_rows;
   const int32_t* n_valid;
   int32_t k;
@@ -324,12 +325,14 @@ struct TopkArgs {
   int32_t kp;         // candidates per block in the workspace: k rounded up to a multiple of 4
   uint32_t* ws_key;   // [n_rows][nblk][kp]
   int32_t* ws_idx;    // [n_rows][nblk][kp]
+  int32_t blk0;       // stage 1: key block of workgroup x = 0
+  int64_t key0;       // stage 1: key at logits[r * ld + 0]
 };
 
 __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
   int nv = a.n_valid ? a.n_valid[r] : (int)a.ld;
   if (nv < 0) nv = 0;
-  if (nv > a.ld) nv = (int)a.ld;
+  if (nv > a.ncap) nv = (int)a.ncap;
   return nv;
 }
 
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(Topk
   __shared__ SelShared sh;
   __shared__ CandShared cs;
   const int r = blockIdx.y;
-  const int bb = blockIdx.x;
+  const int bb = blockIdx.x + a.blk0;
   const int nv = row_valid(a, r);
   if (nv <= a.k) return;  // stage 2 writes the row directly
   const int i0 = bb * a.blk;
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(Topk
   if (n < 0) n = 0;
   uint32_t* ck = a.ws_key + ((int64_t)r * a.nblk + bb) * a.kp;
   int32_t* ci = a.ws_idx + ((int64_t)r * a.nblk + bb) * a.kp;
-  const float* row = a.logits + (int64_t)r * a.ld + i0;
+  const float* row = a.logits + (int64_t)r * a.ld + (i0 - a.key0);
   if (n <= a.k) {
     for (int i = threadIdx.x; i < a.kp; i += kNT) {
       ck[i] = i < n ? order_key(row[i]) : 0u;
@@ -482,6 +485,9 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   TopkArgs a;
   a.logits = logits;
   a.ld = ld;
+  a.ncap = ld;
+  a.blk0 = 0;
+  a.key0 = 0;
   a.n_rows = n_rows;
   a.n_valid = n_valid;
   a.k = k;
@@ -523,6 +529,62 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
     default: launch_stage2<32>(a, st); break;
   }
   return launch_status("tf_topk_blocks");
+}
+
+// ---- key-blocked scoring [CPM, section 2.3]: stage 1 per key block, then the merge --------
+// The caller scores one key block of B keys at a time into a [n_rows][B] buffer; each
+// block's candidates go to its slot of the candidate workspace, and the merge runs once
+// all blocks are in. n_valid holds the rows' full visible counts (clipped to ncap).
+
+size_t topk_cand_bytes(int32_t n_rows, int32_t nb, int32_t k) {
+  return (size_t)n_rows * nb * ((k + 3) / 4 * 4) * 8;
+}
+
+static TopkArgs block_args(const float* logits_blk, int32_t B, int32_t nb, int64_t ncap, int32_t n_rows,
+                           const int32_t* n_valid, int32_t k, int32_t* blocks, void* cand) {
+  TopkArgs a;
+  a.logits = logits_blk;
+  a.ld = B;
+  a.ncap = ncap;
+  a.n_rows = n_rows;
+  a.n_valid = n_valid;
+  a.k = k;
+  a.blocks = blocks;
+  a.vec = B % 4 == 0 && ((uintptr_t)logits_blk & 15) == 0;
+  a.kp = (k + 3) / 4 * 4;
+  a.blk = B;
+  a.nblk = nb;
+  a.ws_key = (uint32_t*)cand;
+  a.ws_idx = (int32_t*)((char*)cand + (size_t)n_rows * nb * a.kp * 4);
+  a.blk0 = 0;
+  a.key0 = 0;
+  return a;
+}
+
+tf_status launch_topk_block(const float* logits_blk, int32_t B, int32_t b, int32_t nb, int64_t ncap,
+                            int32_t n_rows, const int32_t* n_valid, int32_t k, void* cand, hipStream_t st) {
+  TopkArgs a = block_args(logits_blk, B, nb, ncap, n_rows, n_valid, k, nullptr, cand);
+  a.blk0 = b;
+  a.key0 = (int64_t)b * B;
+  switch (run_for(B)) {
+    case 4: hipLaunchKernelGGL(topk_stage1_kernel<4>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(topk_stage1_kernel<8>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(topk_stage1_kernel<16>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
+    default: hipLaunchKernelGGL(topk_stage1_kernel<32>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
+  }
+  return launch_status("tf_indexer_topk");
+}
+
+tf_status launch_topk_merge(int32_t B, int32_t nb, int64_t ncap, int32_t n_rows, const int32_t* n_valid,
+                            int32_t k, int32_t* blocks, void* cand, hipStream_t st) {
+  TopkArgs a = block_args(nullptr, B, nb, ncap, n_rows, n_valid, k, blocks, cand);
+  switch (run_for((int64_t)nb * a.kp)) {
+    case 4: launch_stage2<4>(a, st); break;
+    case 8: launch_stage2<8>(a, st); break;
+    case 16: launch_stage2<16>(a, st); break;
+    default: launch_stage2<32>(a, st); break;
+  }
+  return launch_status("tf_indexer_topk");
 }
 
 }  // namespace tf

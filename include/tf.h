@@ -9,7 +9,9 @@
  *   2. tf_indexer_logits    score query rows against the pooled keys (one per 4
  *                           tokens): l[t,j] = sum_h w[t,h] * ReLU(q[t,h] . k_j),
  *                           fp32, masked causally by the compressed length;
- *   3. tf_topk_blocks       select the top-k pooled blocks of each row;
+ *   3. tf_topk_blocks       select the top-k pooled blocks of each row
+ *                           (tf_indexer_topk runs steps 2 and 3 one key block at
+ *                           a time, without the whole logits buffer);
  *   4. tf_sparse_mla_attn   absorbed-MLA softmax attention that gathers only the
  *                           selected latent rows from the pages (decode rows and
  *                           chunked-prefill rows alike);
@@ -200,6 +202,27 @@ tf_status tf_indexer_logits(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
 tf_status tf_topk_blocks(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                          int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, void* stream);
 size_t tf_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k);
+
+/* Key-blocked indexer + top-k [CPM, section 2.3: score the rows against one key
+ * block at a time, keep each block's top-k with its values, then take the top-k
+ * of the candidates; exact, since topk(union) == topk(union of block top-k)]:
+ * the blocks that tf_indexer_logits followed by tf_topk_blocks would select, bit
+ * for bit, without the [n_rows][ld] logits buffer. Keys [0, ld) are scored in
+ * key_block-key blocks (a multiple of 128 in 128..32768) into a workspace of
+ * n_rows x key_block logits, whose per-block top-k candidates (order keys and
+ * indices) wait in the workspace for the merge. Device memory is
+ * tf_indexer_topk_workspace_bytes(n_rows, ld, k, key_block), flat in ld but
+ * for the candidates (n_rows x blocks x k x 8 bytes). q, w, n_heads and the
+ * masking are as for tf_indexer_logits; blocks, k and the tie rule as for
+ * tf_topk_blocks. n_valid (optional, device int32 [n_rows]) receives n_c.
+ * Limits: n_rows <= 65535, blocks x k <= 32,768 (TF_E_RANGE names the fix).
+ * ws must be 16-byte aligned. The blocks run one after another on `stream`. */
+tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
+                          const int32_t* row_stream, const int32_t* row_pos, const void* q,
+                          const float* w, int32_t n_heads, int64_t ld, int32_t k,
+                          int32_t key_block, int32_t* blocks, int32_t* n_valid, void* ws,
+                          size_t ws_bytes, void* stream);
+size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t key_block);
 
 /* Sparse absorbed-MLA attention [#1313, "Step 2"; #1142, "What stays as it
  * is"]: for row r at position t, head h, with S = {s <= t : s / 4 in

@@ -139,6 +139,22 @@ def test_validation_refuses_before_launch():
     assert "workspace" in L.tf_last_error().decode()
     assert L.tf_dense_mla_attn(ctypes.byref(p), v, 0, None, None, None, 32, 1.0, 64, None, None, None, 0,
                                None) == tf.TF_OK
+    # the key-blocked indexer + top-k: block size, merge capacity, workspace, heads
+    assert L.tf_indexer_topk(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 4096, 64, 200, fake, None, fake,
+                             1 << 30, None) == tf.TF_E_INVAL
+    assert "multiple of 128" in L.tf_last_error().decode()
+    assert L.tf_indexer_topk(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 1 << 20, 2048, 128, fake, None,
+                             fake, 1 << 30, None) == tf.TF_E_RANGE
+    assert "raise key_block" in L.tf_last_error().decode()
+    assert L.tf_indexer_topk(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 4096, 64, 1024, fake, None, fake,
+                             16, None) == tf.TF_E_INVAL
+    assert "workspace" in L.tf_last_error().decode()
+    assert L.tf_indexer_topk(ctypes.byref(p), v, 8, fake, fake, fake, fake, 6, 4096, 64, 1024, fake, None, fake,
+                             1 << 30, None) == tf.TF_E_UNSUPPORTED
+    assert L.tf_indexer_topk(ctypes.byref(p), v, 0, None, None, None, None, 4, 4096, 64, 1024, None, None, None,
+                             0, None) == tf.TF_OK
+    # one block of logits, 4 blocks x 64 candidates x 8 bytes, n_c: per row
+    assert tf.indexer_topk_workspace_bytes(8, 4096, 64, 1024) == 8 * 1024 * 4 + 8 * 4 * 64 * 8 + 32
     # null plan, null pool
     assert L.tf_latent_write(None, v, 1, fake, fake, fake, None, fake, 0, None, None, None, None) == tf.TF_E_INVAL
     nv = tf.tf_kv_view(None, None, 4, 4, 16, 0)

@@ -262,3 +262,36 @@ def test_dense_chunk_full():
         _log(f"dense chunk: oracle on {len(sample)} sampled rows")
         ro, rl = ow.dense_attention(wl, 0, srows, nb, sc)
         check_attention(host(out)[sample], host(lse)[sample], ro, rl, f"dense chunk scale {sc}")
+
+
+def test_indexer_topk_blocked_chunk_full():
+    """T = 2,048 rows against L = 100,000 (25,000 keys) in key blocks of 8,192, as the
+    bench times it: the same blocks as the whole logits buffer and tf_topk_blocks, bit
+    for bit, with 67 MB of block logits in place of 205 MB; sampled rows against the
+    oracle."""
+    wl = prefill_chunk(0)
+    _log("blocked indexer + top-k: populating")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows, ld, k, B = wl.rows, 25000, wl.k, 8192
+    R = len(rows)
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, P.view(), rs, rp, iq, w, logits, n_valid=nv)
+    ref = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    tf.topk_blocks(logits, nv, k, ref)
+    got = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    nv2 = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_topk(plan, P.view(), rs, rp, iq, w, ld, k, B, got, n_valid=nv2)
+    torch.cuda.synchronize()
+    _log("blocked indexer + top-k: equal to the unblocked path")
+    assert torch.equal(nv, nv2)
+    assert torch.equal(got, ref)
+    rng = np.random.default_rng(9)
+    sample = sorted(set([0, 2047] + rng.choice(2048, 6, replace=False).tolist()))
+    srows = [rows[i] for i in sample]
+    _log(f"blocked indexer + top-k: oracle on {len(sample)} sampled rows")
+    ref_l = ow.logits(wl, 0, srows, ld)
+    check_topk_against_oracle(host(got)[sample], ref_l, host(nv)[sample], k)

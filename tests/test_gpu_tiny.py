@@ -558,3 +558,58 @@ def test_dense_fp8_rows(hq):
     out, lse = run_dense(wl, plan, P.view(), rows, 512, 24.0)
     ro, rl = ow.dense_attention(wl, 0, rows, 512, 24.0)
     check_attention(out, lse, ro, rl, "dense fp8")
+
+
+# ---- key-blocked indexer + top-k -----------------------------------------------------
+
+@pytest.mark.parametrize("key_block,k", [(128, 64), (256, 64), (384, 64), (128, 200), (512, 64)])
+def test_indexer_topk_blocked_equals_unblocked(tiny_pool, key_block, k):
+    """Scoring one key block at a time and merging the blocks' top-k gives the blocks
+    the whole logits buffer gives, bit for bit: decode rows, the chunk, and rows that
+    see fewer than k blocks (early positions, a row before the stream's start).
+    Block sizes that divide the 512 keys, one that leaves a ragged last block (384),
+    k above the block size (each block passes all its keys on), one block."""
+    _log(f"indexer + top-k by key blocks of {key_block}, k = {k} (tiny)")
+    wl, plan, P = tiny_pool
+    rows = wl.rows + [(1, 0), (1, 3), (1, 200), (0, 1000), (1, -1)]
+    ld = 512
+    rs, rp, iq, w, q = query_inputs(wl, 0, [(b, max(t, 0)) for b, t in rows])
+    rp[-1] = -1
+    R = len(rows)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, P.view(), rs, rp, iq, w, logits, n_valid=nv)
+    ref = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    tf.topk_blocks(logits, nv, k, ref)
+    got = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    nv2 = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    tf.indexer_topk(plan, P.view(), rs, rp, iq, w, ld, k, key_block, got, n_valid=nv2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(nv2), host(nv))
+    assert np.array_equal(host(got), host(ref))
+    blk = host(got)
+    assert np.all(blk[-1] == -1)
+    # and against the oracle's logits (the checks of the unblocked path)
+    ref_l = ow.logits(wl, 0, [(b, max(t, 0)) for b, t in rows[:-1]], ld)
+    check_topk_against_oracle(blk[:-1], ref_l, host(nv)[:-1], k)
+
+
+def test_indexer_topk_blocked_without_n_valid_and_reused_workspace(tiny_pool):
+    """No n_valid output (the library keeps n_c in the workspace); one workspace for two
+    calls in a row, the second on fewer rows."""
+    _log("indexer + top-k by key blocks: workspace n_c, reused workspace (tiny)")
+    wl, plan, P = tiny_pool
+    ld, k, B = 512, 64, 128
+    ws = torch.empty(tf.indexer_topk_workspace_bytes(len(wl.rows), ld, k, B), dtype=torch.uint8, device="cuda")
+    for rows in (wl.rows, wl.rows[:40]):
+        rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+        R = len(rows)
+        logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+        nv = torch.empty(R, dtype=torch.int32, device="cuda")
+        tf.indexer_logits(plan, P.view(), rs, rp, iq, w, logits, n_valid=nv)
+        ref = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        tf.topk_blocks(logits, nv, k, ref)
+        got = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        tf.indexer_topk(plan, P.view(), rs, rp, iq, w, ld, k, B, got, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got), host(ref))
