@@ -169,7 +169,7 @@ extern "C" tf_status tf_indexer_logits(const tf_plan* p, tf_kv_view keys, int32_
     return set_error(TF_E_INVAL, "tf_indexer_logits: row_stream, row_pos, q, w and logits are required");
   if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_indexer_logits: q must be 16-byte aligned");
   return launch_indexer(p, make_view(p, keys), n_rows, row_stream, row_pos, q, w, n_heads, logits, ld,
-                        n_valid, (hipStream_t)stream, 0, ld, ld);
+                        n_valid, (hipStream_t)stream, 0, ld, ld, false);
 }
 
 extern "C" size_t tf_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k) {
@@ -245,7 +245,7 @@ extern "C" tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t 
   for (int64_t b = 0; b < nb; ++b) {
     const int64_t k0 = b * key_block, k1 = k0 + key_block < ld ? k0 + key_block : ld;
     if ((s = launch_indexer(p, v, n_rows, row_stream, row_pos, q, w, n_heads, lbuf, key_block, b == 0 ? nv : nullptr,
-                            st, k0, k1, ld)) != TF_OK)
+                            st, k0, k1, ld, true)) != TF_OK)
       return s;
     if ((s = launch_topk_block(lbuf, key_block, (int32_t)b, (int32_t)nb, ld, n_rows, nv, k, cand, st)) != TF_OK)
       return s;

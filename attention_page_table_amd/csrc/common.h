@@ -61,11 +61,13 @@ tf_status launch_snapshot(const tf_plan* p, const tf_kv_view& src, const tf_kv_v
                           int32_t n_streams, const int32_t* src_stream, const int32_t* dst_stream,
                           int64_t at, hipStream_t st);
 // Scores keys [key0, kend) into logits[row * ld + (key - key0)]; n_c is clipped to
-// ncap (the whole call: key0 = 0, kend = ncap = ld).
+// ncap (the whole call: key0 = 0, kend = ncap = ld). `window`: one key block of a
+// key-blocked call (its own kernel instance, same code).
 tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows,
                          const int32_t* row_stream, const int32_t* row_pos, const void* q,
                          const float* w, int32_t n_heads, float* logits, int64_t ld,
-                         int32_t* n_valid, hipStream_t st, int64_t key0, int64_t kend, int64_t ncap);
+                         int32_t* n_valid, hipStream_t st, int64_t key0, int64_t kend, int64_t ncap,
+                         bool window);
 size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k);
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                       int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st);

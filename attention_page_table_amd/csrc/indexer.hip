@@ -188,7 +188,9 @@ __device__ __forceinline__ int swz(int j, int c) {
   return j * CH + (c ^ (j & (CH - 1)));
 }
 
-template <int H, int D, int MT>
+// WINDOW names the instance that scores one key block of a key-blocked call, so that
+// profiles keep its launches apart from whole-range ones; the code is the same.
+template <int H, int D, int MT, bool WINDOW>
 __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   constexpr int RPT = 32 / H;   // query rows per MFMA tile
   constexpr int RH = 16 / H;    // rows per half-wave in the accumulators
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 }
 
 template <int H, int D>
-static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
+static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st, bool window) {
   constexpr int RPT = 32 / H;
   if (n_rows >= 64) {
     constexpr int MT = 2;
@@ -439,8 +441,12 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
     const int64_t kgroups = (nk + kpw - 1) / kpw;
     a.n_kgroups = (int32_t)kgroups;
     if (rgroups > 65535) return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows for one launch");
-    hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT>), dim3((unsigned)kgroups, (unsigned)rgroups), dim3(256), 0,
-                       st, a);
+    if (window)
+      hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, true>), dim3((unsigned)kgroups, (unsigned)rgroups),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, false>), dim3((unsigned)kgroups, (unsigned)rgroups),
+                         dim3(256), 0, st, a);
   } else {
     // each wave one row; about 2,048 waves in all (eight per CU keep more key loads in
     // flight than four); a wave's range spans at most 64 pages
@@ -463,7 +469,7 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st) {
 tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
                          const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
                          float* logits, int64_t ld, int32_t* n_valid, hipStream_t st, int64_t key0,
-                         int64_t kend, int64_t ncap) {
+                         int64_t kend, int64_t ncap, bool window) {
   IdxArgs a;
   a.v = v;
   a.off_pkey = p->off_pkey;
@@ -484,13 +490,13 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, con
   const int D = p->g.index_dim;
   tf_status s;
   if (D == 128) {
-    if (n_heads == 16) s = launch_hd<16, 128>(a, n_rows, st);
-    else if (n_heads == 8) s = launch_hd<8, 128>(a, n_rows, st);
-    else s = launch_hd<4, 128>(a, n_rows, st);
+    if (n_heads == 16) s = launch_hd<16, 128>(a, n_rows, st, window);
+    else if (n_heads == 8) s = launch_hd<8, 128>(a, n_rows, st, window);
+    else s = launch_hd<4, 128>(a, n_rows, st, window);
   } else {
-    if (n_heads == 16) s = launch_hd<16, 64>(a, n_rows, st);
-    else if (n_heads == 8) s = launch_hd<8, 64>(a, n_rows, st);
-    else s = launch_hd<4, 64>(a, n_rows, st);
+    if (n_heads == 16) s = launch_hd<16, 64>(a, n_rows, st, window);
+    else if (n_heads == 8) s = launch_hd<8, 64>(a, n_rows, st, window);
+    else s = launch_hd<4, 64>(a, n_rows, st, window);
   }
   if (s != TF_OK) return s;
   return launch_status("tf_indexer_logits");

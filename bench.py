@@ -21,6 +21,8 @@ Reported:
   traffic the rocprofv3 counters measured for it when they match the source;
 * the prefill-chunk indexer (T = 2,048 rows against 25,000 pooled keys) against
   the bf16 MFMA roofline, and the whole prefill-chunk step call by call;
+* the same chunk's indexer and top-k by key blocks (tf_indexer_topk), against the
+  whole-buffer calls;
 * the dense pass (no indexer or top-k) over a 2,048-row chunk at L = 4,096;
 * the oracle timed on the host cores on a bounded sample of the same step.
 
@@ -58,7 +60,7 @@ CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
 ENTRIES = {
     "write": (("tf::latent_write_kernel",), "write.hip"),
     "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
-    "indexer_prefill": (("tf::indexer_tile_kernel",), "indexer.hip"),
+    "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, false>",), "indexer.hip"),
     "topk": (("tf::topk_stage1_kernel", "tf::topk_stage2_kernel"), "topk.hip"),
     "topk_prefill": (("tf::topk_row_kernel",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
@@ -435,8 +437,39 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
                           "roofline": mfma(attn_flop, us["attention"])},
         },
         "quantizing_write": bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm),
+        "blocked_indexer_topk": bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, blocks, reps,
+                                                           idx_flop, us["indexer"] + us["topk"], mfma),
     }
     return res
+
+
+def bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, ref_blocks, reps, flop, unblocked_us,
+                               mfma, key_block=8192):
+    """The same chunk's logits and top-512 by key blocks (tf_indexer_topk): each block of
+    8,192 keys scored into a flat workspace, its top-k candidates kept, one merge. Its
+    device memory against the whole [T, 25,000] logits buffer, and its time against the
+    indexer and top-k calls of the step; the result is checked equal to the step's."""
+    import numpy as np
+    import torch
+    T, ld = logits.shape
+    k = ref_blocks.shape[1]
+    got = torch.empty_like(ref_blocks)
+    ws_bytes = tf.indexer_topk_workspace_bytes(T, ld, k, key_block)
+    f = tf.indexer_topk(plan, view, rs, rp, iq, w, ld, k, key_block, got, prepare=True)
+    f()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_blocks), "key-blocked top-k differs from the whole-buffer top-k"
+    ev = [TimingEvent() for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        f()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+    return {"call": "tf_indexer_topk", "key_block": key_block, "blocks": (ld + key_block - 1) // key_block,
+            "us": round(us, 2), "unblocked_indexer_plus_topk_us": round(unblocked_us, 2),
+            "workspace_bytes": ws_bytes, "unblocked_logits_bytes": T * ld * 4, "causal_flop": flop,
+            "roofline": mfma(flop, us), "equal_to_unblocked": True}
 
 
 def bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm):
