@@ -61,7 +61,7 @@ ENTRIES = {
     "write": (("tf::latent_write_kernel",), "write.hip"),
     "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
     "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, false>",), "indexer.hip"),
-    "topk": (("tf::topk_stage1_kernel", "tf::topk_stage2_kernel"), "topk.hip"),
+    "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4>"), "topk.hip"),
     "topk_prefill": (("tf::topk_row_kernel",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
     "attention_prefill": (("tf::attn_kernel",), "attention.hip"),
