@@ -34,7 +34,7 @@ from .layout import Geom, BlockLayout, block_layout, page_bytes, PoolImage  # no
 from .plan import bytes_per_token, bytes_per_token_rank, kv_pool_plan, Plan  # noqa: F401
 from .schedule import chunk_size, chunk_schedule  # noqa: F401
 from .indexer import n_compressed, indexer_logits  # noqa: F401
-from .topk import topk_blocks  # noqa: F401
+from .topk import topk_blocks, candidate_groups, topk_in_candidates  # noqa: F401
 from .attention import selected_tokens, sparse_mla_row, sparse_mla  # noqa: F401
 from .attention import dense_tokens, dense_mla_row, dense_mla  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode_nearest, quantize_rows  # noqa: F401

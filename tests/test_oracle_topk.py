@@ -63,3 +63,55 @@ def test_blocked_merge_identity():
         merged = cand[sub[sub >= 0]]
         direct = topk_row(v, n, k)
         assert np.array_equal(np.sort(merged), direct[direct >= 0])
+
+
+# ---- two-level candidate selection: groups of g keys, top-n_cand groups, then top-k ----
+
+from oracle import candidate_groups, topk_in_candidates  # noqa: E402
+
+
+def test_candidates_worked_example():
+    # 19 visible keys in groups of 8: {0..7}, {8..15}, {16..18} (key 19 is not visible)
+    v = np.array([0, 1, 2, 3, 4, 5, 6, 7,  9, 0, 0, 0, 0, 0, 0, 0,  8, 8, 1, 99], dtype=float)
+    # group scores 7, 9, 8 -> the best group is 1, the best two are 1 and 2
+    assert candidate_groups(v[None], [19], 8, 1).tolist() == [[1]]
+    assert candidate_groups(v[None], [19], 8, 2).tolist() == [[1, 2]]
+    assert candidate_groups(v[None], [19], 8, 5).tolist() == [[0, 1, 2, -1, -1]]
+    # inside groups 1 and 2 the top three keys are 8 (9), 16 and 17 (8 each)
+    assert topk_in_candidates(v[None], [19], [[1, 2]], 8, 3).tolist() == [[8, 16, 17]]
+    # only group 1 kept: its key 8 (9), then its zeros by index (9, 10)
+    assert topk_in_candidates(v[None], [19], [[1, -1]], 8, 3).tolist() == [[8, 9, 10]]
+    # more keys wanted than the candidates hold: the -inf keys follow by index
+    assert topk_in_candidates(v[None], [19], [[2]], 8, 5).tolist() == [[0, 1, 16, 17, 18]]
+
+
+def test_group_of_one_is_plain_topk():
+    rng = np.random.default_rng(5)
+    v = rng.integers(-3, 4, size=(6, 50)).astype(float)
+    nv = [50, 49, 17, 1, 30, 8]
+    for k in (1, 5, 20, 60):
+        assert np.array_equal(candidate_groups(v, nv, 1, k), topk_blocks(v, nv, k))
+
+
+def test_all_groups_candidates_is_plain_topk():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((5, 64))
+    nv = [64, 63, 9, 40, 1]
+    cand = candidate_groups(v, nv, 8, 8)                 # every group of every row
+    for k in (1, 7, 30):
+        assert np.array_equal(topk_in_candidates(v, nv, cand, 8, k), topk_blocks(v, nv, k))
+
+
+def test_candidates_brute_force_with_ties():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(rng.integers(1, 60))
+        g = int(rng.choice([1, 2, 3, 8]))
+        nc = int(rng.integers(1, 10))
+        k = int(rng.integers(1, 20))
+        vals = rng.integers(-3, 4, size=n).astype(float)
+        scores = [max(float(vals[j]) for j in range(s, min(s + g, n))) for s in range(0, n, g)]
+        cand = brute(scores, len(scores), nc)
+        assert candidate_groups(vals[None], [n], g, nc)[0].tolist() == cand, trial
+        masked = [float(vals[j]) if j // g in cand else -np.inf for j in range(n)]
+        assert topk_in_candidates(vals[None], [n], [cand], g, k)[0].tolist() == brute(masked, n, k), trial
