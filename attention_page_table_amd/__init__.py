@@ -65,6 +65,11 @@ SIGNATURES = {
     "tf_indexer_topk": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32, _c_i64,
                                  _c_i32, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_indexer_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
+    "tf_candidate_groups": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_candidate_groups_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
+    "tf_topk_in_candidates": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp,
+                                       ctypes.c_size_t, _vp]),
+    "tf_topk_in_candidates_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32]),
     "tf_dense_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
                                    ctypes.c_float, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_attn_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
@@ -225,6 +230,28 @@ def indexer_topk(plan, keys, row_stream, row_pos, q, w, ld: int, k: int, key_blo
     return _run("tf_indexer_topk", (ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
                                     _ptr(w), H, int(ld), int(k), int(key_block), _ptr(blocks), _ptr(n_valid),
                                     _ptr(ws), ws.numel(), _stream(stream)), prepare, keep=(ws,))
+
+
+def candidate_groups(logits, n_valid, group: int, n_cand: int, cand, ws=None, stream=None, prepare=False):
+    n_rows, ld = logits.shape
+    if ws is None:
+        import torch
+        need = int(lib().tf_candidate_groups_workspace_bytes(n_rows, ld, group, n_cand))
+        ws = torch.empty(max(16, need), dtype=torch.uint8, device=logits.device)
+    return _run("tf_candidate_groups", (_ptr(logits), ld, n_rows, _ptr(n_valid), int(group), int(n_cand), _ptr(cand),
+                                        _ptr(ws), ws.numel(), _stream(stream)), prepare, keep=(ws,))
+
+
+def topk_in_candidates(logits, n_valid, cand, group: int, k: int, blocks, ws=None, stream=None, prepare=False):
+    """Masks logits in place (keys outside the candidate groups become -inf), then top-k."""
+    n_rows, ld = logits.shape
+    need = int(lib().tf_topk_in_candidates_workspace_bytes(n_rows, ld, k))
+    if need and ws is None:
+        import torch
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    return _run("tf_topk_in_candidates", (_ptr(logits), ld, n_rows, _ptr(n_valid), _ptr(cand), cand.shape[1],
+                                          int(group), int(k), _ptr(blocks), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(stream)), prepare, keep=(ws,))
 
 
 def attn_workspace_bytes(n_rows: int, n_heads: int, k: int) -> int:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "plan.cpp", "write.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "write.hip", "indexer.hip", "topk.hip", "candidates.hip", "attention.hip"]
 LIB = os.path.join(HERE, "libtf.so")
 SYNTH_SRC = os.path.join(ROOT, "synth", "synth.hip")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libtf_synth.so")

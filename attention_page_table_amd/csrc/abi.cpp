@@ -253,6 +253,84 @@ extern "C" tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t 
   return launch_topk_merge(key_block, (int32_t)nb, ld, n_rows, nv, k, blocks, cand, st);
 }
 
+// Candidate groups' workspace: the group scores (rows padded to whole quads), the
+// rows' group counts, then the top-k's own.
+static int64_t group_stride(int64_t ld, int32_t g) { return ((ld + g - 1) / g + 3) / 4 * 4; }
+
+static size_t cand_ws(int32_t n_rows, int64_t ld, int32_t g, int32_t n_cand, size_t* topk_part) {
+  const int64_t ldg = group_stride(ld, g);
+  const size_t t = topk_ws_bytes(n_rows, ldg, n_cand);
+  if (topk_part) *topk_part = t;
+  if (t == (size_t)-1) return t;
+  return (size_t)n_rows * ldg * 4 + ((size_t)n_rows * 4 + 15) / 16 * 16 + t;
+}
+
+extern "C" size_t tf_candidate_groups_workspace_bytes(int32_t n_rows, int64_t ld, int32_t group, int32_t n_cand) {
+  if (n_rows <= 0 || ld <= 0 || group <= 0 || n_cand <= 0) return 0;
+  return cand_ws(n_rows, ld, group, n_cand, nullptr);
+}
+
+extern "C" tf_status tf_candidate_groups(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+                                         int32_t group, int32_t n_cand, int32_t* cand, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  clear_error();
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_candidate_groups: n_rows < 0");
+  if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_candidate_groups: n_rows=%d, at most 65535 a call", n_rows);
+  if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_candidate_groups: ld=%lld", (long long)ld);
+  if (group < 1 || group > 64) return set_error(TF_E_RANGE, "tf_candidate_groups: group=%d, need 1..64", group);
+  if (n_cand < 1 || n_cand > 2048)
+    return set_error(TF_E_RANGE, "tf_candidate_groups: n_cand=%d, need 1..2048", n_cand);
+  if (n_rows == 0) return TF_OK;
+  if (!logits || !cand) return set_error(TF_E_INVAL, "tf_candidate_groups: logits and cand are required");
+  size_t tpart = 0;
+  const size_t need = cand_ws(n_rows, ld, group, n_cand, &tpart);
+  if (need == (size_t)-1)
+    return set_error(TF_E_UNSUPPORTED, "tf_candidate_groups: %lld groups with n_cand=%d exceed the blocked merge",
+                     (long long)((ld + group - 1) / group), n_cand);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return set_error(TF_E_INVAL, "tf_candidate_groups: a 16-byte aligned workspace of %zu bytes is needed, got %zu",
+                     need, ws_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t ldg = group_stride(ld, group);
+  float* scores = (float*)ws;
+  int32_t* ngroups = (int32_t*)((char*)ws + (size_t)n_rows * ldg * 4);
+  void* tws = tpart ? (char*)ngroups + ((size_t)n_rows * 4 + 15) / 16 * 16 : nullptr;
+  tf_status s = launch_group_max(logits, ld, n_rows, n_valid, group, scores, ldg, ngroups, st);
+  if (s != TF_OK) return s;
+  return launch_topk(scores, ldg, n_rows, ngroups, n_cand, cand, tws, tpart, st);
+}
+
+extern "C" size_t tf_topk_in_candidates_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k) {
+  return tf_topk_workspace_bytes(n_rows, ld, k);
+}
+
+extern "C" tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+                                           const int32_t* cand, int32_t n_cand, int32_t group, int32_t k,
+                                           int32_t* blocks, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_topk_in_candidates: n_rows < 0");
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_topk_in_candidates: k=%d, need 1..2048", k);
+  if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_topk_in_candidates: ld=%lld", (long long)ld);
+  if (group < 1 || group > 64) return set_error(TF_E_RANGE, "tf_topk_in_candidates: group=%d, need 1..64", group);
+  if (n_cand < 1) return set_error(TF_E_RANGE, "tf_topk_in_candidates: n_cand=%d, need >= 1", n_cand);
+  if ((ld + group - 1) / group > cand_max_groups())
+    return set_error(TF_E_RANGE, "tf_topk_in_candidates: %lld groups, the candidate bitmap holds %lld",
+                     (long long)((ld + group - 1) / group), (long long)cand_max_groups());
+  if (n_rows == 0) return TF_OK;
+  if (!logits || !cand || !blocks)
+    return set_error(TF_E_INVAL, "tf_topk_in_candidates: logits, cand and blocks are required");
+  const size_t need = topk_ws_bytes(n_rows, ld, k);
+  if (need == (size_t)-1)
+    return set_error(TF_E_UNSUPPORTED, "tf_topk_in_candidates: ld=%lld with k=%d exceeds the blocked merge",
+                     (long long)ld, k);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return set_error(TF_E_INVAL, "tf_topk_in_candidates: workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  tf_status s = launch_mask(logits, ld, n_rows, n_valid, cand, n_cand, group, st);
+  if (s != TF_OK) return s;
+  return launch_topk(logits, ld, n_rows, n_valid, k, blocks, ws, ws_bytes, st);
+}
+
 extern "C" size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {
   if (n_rows <= 0 || n_heads <= 0 || k <= 0) return 0;
   return attn_ws_bytes(n_rows, n_heads, k);

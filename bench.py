@@ -22,7 +22,8 @@ Reported:
 * the prefill-chunk indexer (T = 2,048 rows against 25,000 pooled keys) against
   the bf16 MFMA roofline, and the whole prefill-chunk step call by call;
 * the same chunk's indexer and top-k by key blocks (tf_indexer_topk), against the
-  whole-buffer calls;
+  whole-buffer calls, and its two-level candidate selection (top-2,048 groups of 8
+  keys, then top-512 inside them);
 * the dense pass (no indexer or top-k) over a 2,048-row chunk at L = 4,096;
 * the oracle timed on the host cores on a bounded sample of the same step.
 
@@ -439,8 +440,50 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
         "quantizing_write": bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm),
         "blocked_indexer_topk": bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, blocks, reps,
                                                            idx_flop, us["indexer"] + us["topk"], mfma),
+        "candidate_selection": bench_candidates(tf, logits, nv, pw.k, reps, hbm),
     }
     return res
+
+
+def bench_candidates(tf, logits, nv, k, reps, hbm, group=8, n_cand=2048):
+    """Two-level selection on the chunk's logits: the candidate layer's top-2,048 groups
+    of 8 keys (tf_candidate_groups: reads the logits, writes the group maxima, selects),
+    then a consumer's top-512 inside them (tf_topk_in_candidates on a copy: masks the
+    non-candidates in place, selects). The consumer is timed on the same copy again
+    and again: masking writes the same -inf quads each time. Algorithmic bytes: the
+    logits read and the group maxima written; the -inf quads written and the logits
+    read."""
+    import numpy as np
+    import torch
+    T, ld = logits.shape
+    cand = torch.empty((T, n_cand), dtype=torch.int32, device="cuda")
+    f1 = tf.candidate_groups(logits, nv, group, n_cand, cand, prepare=True)
+    work = logits.clone()
+    blk = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    f2 = tf.topk_in_candidates(work, nv, cand, group, k, blk, prepare=True)
+    f1()
+    f2()
+    torch.cuda.synchronize()
+    res = {}
+    for name, f in (("candidate_groups", f1), ("topk_in_candidates", f2)):
+        ev = [TimingEvent() for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+    nvh = nv.cpu().numpy().astype(np.int64)
+    n_groups = (nvh + group - 1) // group
+    masked_keys = int(np.maximum(0, nvh - group * np.minimum(n_groups, n_cand)).sum())
+    b1 = int(nvh.sum()) * 4 + int(n_groups.sum()) * 4
+    b2 = masked_keys * 4 + int(nvh.sum()) * 4
+    del work
+    return {"group": group, "n_cand": n_cand, "k": k,
+            "candidate_groups": {"us": round(res["candidate_groups"], 2), "alg_bytes": b1,
+                                 "roofline": hbm(b1, res["candidate_groups"])},
+            "topk_in_candidates": {"us": round(res["topk_in_candidates"], 2), "alg_bytes": b2,
+                                   "roofline": hbm(b2, res["topk_in_candidates"])}}
 
 
 def bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, ref_blocks, reps, flop, unblocked_us,

@@ -11,7 +11,9 @@
  *                           fp32, masked causally by the compressed length;
  *   3. tf_topk_blocks       select the top-k pooled blocks of each row
  *                           (tf_indexer_topk runs steps 2 and 3 one key block at
- *                           a time, without the whole logits buffer);
+ *                           a time, without the whole logits buffer;
+ *                           tf_candidate_groups and tf_topk_in_candidates select
+ *                           in two levels, candidate groups then keys);
  *   4. tf_sparse_mla_attn   absorbed-MLA softmax attention that gathers only the
  *                           selected latent rows from the pages (decode rows and
  *                           chunked-prefill rows alike);
@@ -223,6 +225,36 @@ tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
                           int32_t key_block, int32_t* blocks, int32_t* n_valid, void* ws,
                           size_t ws_bytes, void* stream);
 size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t key_block);
+
+/* Two-level candidate selection [CPM, section 1: a layer publishes candidate
+ * masks that the later low-ratio layers consume; section 2.3: its block pooling
+ * over 8-key groups and top-2,048 groups, and the consumers' masking of
+ * non-candidates before their own top-k]. The pages name the steps only; the
+ * readings taken:
+ *
+ * tf_candidate_groups: each visible group of `group` consecutive keys (keys
+ * j < n_valid[r]; the last group may be partial) scores the largest of its
+ * logits, and cand [n_rows][n_cand] receives the top-n_cand groups of each row
+ * as tf_topk_blocks selects (ties to the lower group, ascending, -1 padded).
+ * logits are read only. 1 <= group <= 64, 1 <= n_cand <= 2048, n_rows <= 65535.
+ * ws: 16-byte aligned device workspace of at least
+ * tf_candidate_groups_workspace_bytes(n_rows, ld, group, n_cand) bytes.
+ *
+ * tf_topk_in_candidates: the consumer. The visible keys of row r outside its
+ * candidate groups (cand [n_rows][n_cand], entries < 0 ignored) are set to
+ * -inf IN PLACE in logits, as the pages' masked_fill_ does, and blocks receives
+ * the row's top-k as tf_topk_blocks selects it from the masked row (fewer than
+ * k candidate keys: the lowest-index others complete it). Keys at or past
+ * n_valid are not touched. At most 262,144 groups a row. ws: as for
+ * tf_topk_blocks (tf_topk_in_candidates_workspace_bytes). */
+tf_status tf_candidate_groups(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+                              int32_t group, int32_t n_cand, int32_t* cand, void* ws, size_t ws_bytes,
+                              void* stream);
+size_t tf_candidate_groups_workspace_bytes(int32_t n_rows, int64_t ld, int32_t group, int32_t n_cand);
+tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+                                const int32_t* cand, int32_t n_cand, int32_t group, int32_t k,
+                                int32_t* blocks, void* ws, size_t ws_bytes, void* stream);
+size_t tf_topk_in_candidates_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k);
 
 /* Sparse absorbed-MLA attention [#1313, "Step 2"; #1142, "What stays as it
  * is"]: for row r at position t, head h, with S = {s <= t : s / 4 in

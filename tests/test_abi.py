@@ -155,6 +155,19 @@ def test_validation_refuses_before_launch():
                              0, None) == tf.TF_OK
     # one block of logits, 4 blocks x 64 candidates x 8 bytes, n_c: per row
     assert tf.indexer_topk_workspace_bytes(8, 4096, 64, 1024) == 8 * 1024 * 4 + 8 * 4 * 64 * 8 + 32
+    # two-level candidate selection: group size, candidate count, bitmap capacity, workspace
+    assert L.tf_candidate_groups(fake, 25000, 8, None, 0, 2048, fake, fake, 1 << 30, None) == tf.TF_E_RANGE
+    assert L.tf_candidate_groups(fake, 25000, 8, None, 8, 4096, fake, fake, 1 << 30, None) == tf.TF_E_RANGE
+    assert L.tf_candidate_groups(fake, 25000, 8, None, 8, 2048, fake, fake, 16, None) == tf.TF_E_INVAL
+    assert "workspace" in L.tf_last_error().decode()
+    assert L.tf_candidate_groups(fake, 25000, 0, None, 8, 2048, None, None, 0, None) == tf.TF_OK
+    assert L.tf_topk_in_candidates(fake, 1 << 22, 8, None, fake, 2048, 8, 512, fake, fake, 1 << 30,
+                                   None) == tf.TF_E_RANGE
+    assert "bitmap" in L.tf_last_error().decode()
+    assert L.tf_topk_in_candidates(fake, 25000, 8, None, fake, 2048, 65, 512, fake, fake, 1 << 30,
+                                   None) == tf.TF_E_RANGE
+    assert L.tf_topk_in_candidates(fake, 25000, 8, None, None, 2048, 8, 512, fake, fake, 1 << 30,
+                                   None) == tf.TF_E_INVAL
     # null plan, null pool
     assert L.tf_latent_write(None, v, 1, fake, fake, fake, None, fake, 0, None, None, None, None) == tf.TF_E_INVAL
     nv = tf.tf_kv_view(None, None, 4, 4, 16, 0)

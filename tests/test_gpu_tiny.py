@@ -616,3 +616,42 @@ def test_indexer_topk_blocked_without_n_valid_and_reused_workspace(tiny_pool):
         tf.indexer_topk(plan, P.view(), rs, rp, iq, w, ld, k, B, got, ws=ws)
         torch.cuda.synchronize()
         assert np.array_equal(host(got), host(ref))
+
+
+# ---- two-level candidate selection ---------------------------------------------------
+
+@pytest.mark.parametrize("group,n_cand,k", [(8, 64, 40), (8, 2048, 512), (3, 50, 60), (1, 100, 100), (8, 5, 64)])
+def test_candidate_selection_against_oracle(group, n_cand, k):
+    """Groups of 8 (quads), 3 (no quads) and 1 (plain top-k), ragged rows whose last group
+    is partial, a row before the stream's start, tied values; consumers with more
+    candidate keys than k and with fewer (n_cand 5 x 8 keys < 64: completed by the
+    lowest-index others). Exact against the oracle on the same fp32 values."""
+    from oracle import candidate_groups as o_cand, topk_in_candidates as o_topk
+    _log(f"candidate selection: groups of {group}, {n_cand} candidates, top-{k}")
+    rng = np.random.default_rng(group * 1000 + n_cand)
+    R, ld = 140, 20000 if n_cand == 2048 else 3000
+    v = rng.standard_normal((R, ld)).astype(np.float32)
+    v[::3] = np.round(v[::3], 1)                               # heavy ties on every third row
+    nv = rng.integers(1, ld + 1, size=R).astype(np.int32)
+    nv[0], nv[1], nv[2], nv[3] = ld, ld - 1, 0, 7
+    lg = torch.from_numpy(v).cuda()
+    nvt = torch.from_numpy(nv).cuda()
+    cand = torch.full((R, n_cand), -7, dtype=torch.int32, device="cuda")
+    tf.candidate_groups(lg, nvt, group, n_cand, cand)
+    blk = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    lg2 = lg.clone()
+    tf.topk_in_candidates(lg2, nvt, cand, group, k, blk)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, torch.from_numpy(v).cuda())        # the candidate call only reads
+    ref_c = o_cand(v, nv, group, n_cand)
+    assert np.array_equal(host(cand), ref_c)
+    assert np.array_equal(host(blk), o_topk(v, nv, ref_c, group, k))
+    # masked in place: visible non-candidates are -inf, the rest unchanged
+    m = host(lg2)
+    for r in (0, 1, 4, 5):
+        keep = np.zeros(ld, dtype=bool)
+        for c in ref_c[r][ref_c[r] >= 0]:
+            keep[c * group:(c + 1) * group] = True
+        vis = np.arange(ld) < nv[r]
+        assert np.all(m[r][vis & ~keep] == -np.inf)
+        assert np.array_equal(m[r][~(vis & ~keep)], v[r][~(vis & ~keep)])
