@@ -243,7 +243,7 @@ def candidate_groups(logits, n_valid, group: int, n_cand: int, cand, ws=None, st
 
 
 def topk_in_candidates(logits, n_valid, cand, group: int, k: int, blocks, ws=None, stream=None, prepare=False):
-    """Masks logits in place (keys outside the candidate groups become -inf), then top-k."""
+    """Top-k of each row with its keys outside the candidate groups read as -inf."""
     n_rows, ld = logits.shape
     need = int(lib().tf_topk_in_candidates_workspace_bytes(n_rows, ld, k))
     if need and ws is None:

@@ -304,7 +304,7 @@ extern "C" size_t tf_topk_in_candidates_workspace_bytes(int32_t n_rows, int64_t 
   return tf_topk_workspace_bytes(n_rows, ld, k);
 }
 
-extern "C" tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+extern "C" tf_status tf_topk_in_candidates(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                                            const int32_t* cand, int32_t n_cand, int32_t group, int32_t k,
                                            int32_t* blocks, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
@@ -313,9 +313,6 @@ extern "C" tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_
   if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_topk_in_candidates: ld=%lld", (long long)ld);
   if (group < 1 || group > 64) return set_error(TF_E_RANGE, "tf_topk_in_candidates: group=%d, need 1..64", group);
   if (n_cand < 1) return set_error(TF_E_RANGE, "tf_topk_in_candidates: n_cand=%d, need >= 1", n_cand);
-  if ((ld + group - 1) / group > cand_max_groups())
-    return set_error(TF_E_RANGE, "tf_topk_in_candidates: %lld groups, the candidate bitmap holds %lld",
-                     (long long)((ld + group - 1) / group), (long long)cand_max_groups());
   if (n_rows == 0) return TF_OK;
   if (!logits || !cand || !blocks)
     return set_error(TF_E_INVAL, "tf_topk_in_candidates: logits, cand and blocks are required");
@@ -325,10 +322,8 @@ extern "C" tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_
                      (long long)ld, k);
   if (need > 0 && (!ws || ws_bytes < need))
     return set_error(TF_E_INVAL, "tf_topk_in_candidates: workspace of %zu bytes needed, got %zu", need, ws_bytes);
-  const hipStream_t st = (hipStream_t)stream;
-  tf_status s = launch_mask(logits, ld, n_rows, n_valid, cand, n_cand, group, st);
-  if (s != TF_OK) return s;
-  return launch_topk(logits, ld, n_rows, n_valid, k, blocks, ws, ws_bytes, st);
+  return launch_topk(logits, ld, n_rows, n_valid, k, blocks, ws, ws_bytes, (hipStream_t)stream, cand, n_cand,
+                     group);
 }
 
 extern "C" size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {

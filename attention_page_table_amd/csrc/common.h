@@ -69,8 +69,10 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows,
                          int32_t* n_valid, hipStream_t st, int64_t key0, int64_t kend, int64_t ncap,
                          bool window);
 size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k);
+// cand (nullable): keys outside the row's candidate groups of `group` keys read as -inf
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
-                      int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st);
+                      int32_t k, int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st,
+                      const int32_t* cand = nullptr, int32_t n_cand = 0, int32_t group = 1);
 // key-blocked top-k: stage 1 of key block b (logits_blk is [n_rows][B]), then the merge
 size_t topk_cand_bytes(int32_t n_rows, int32_t nb, int32_t k);
 tf_status launch_topk_block(const float* logits_blk, int32_t B, int32_t b, int32_t nb, int64_t ncap,
@@ -78,11 +80,8 @@ tf_status launch_topk_block(const float* logits_blk, int32_t B, int32_t b, int32
 tf_status launch_topk_merge(int32_t B, int32_t nb, int64_t ncap, int32_t n_rows, const int32_t* n_valid,
                             int32_t k, int32_t* blocks, void* cand, hipStream_t st);
 // two-level candidate selection (candidates.hip)
-int64_t cand_max_groups();
 tf_status launch_group_max(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid, int32_t g,
                            float* scores, int64_t ldg, int32_t* n_groups, hipStream_t st);
-tf_status launch_mask(float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid, const int32_t* cand,
-                      int32_t n_cand, int32_t g, hipStream_t st);
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
 // blocks == nullptr runs the dense pass over the first k pooled blocks
 tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,

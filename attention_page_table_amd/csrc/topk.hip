@@ -328,7 +328,67 @@ struct TopkArgs {
   int32_t* ws_idx;    // [n_rows][nblk][kp]
   int32_t blk0;       // stage 1: key block of workgroup x = 0
   int64_t key0;       // stage 1: key at logits[r * ld + 0]
+  const int32_t* cand;   // masked kernels: [n_rows][n_cand] candidate groups of `group` keys
+  int32_t n_cand;
+  int32_t group;
 };
+
+// Candidate bitmap of the masked kernels: the groups of one segment (at most 32,768 keys).
+constexpr int kMaskWords = 32768 / 32 + 2;
+
+// Masked kernels: the candidate groups among [g0, g0 + ng) as bits, from row r's list.
+__device__ __forceinline__ void load_candidates(const TopkArgs& a, int r, int64_t g0, int ng, uint32_t* bits) {
+  for (int i = threadIdx.x; i < (ng + 31) / 32; i += kNT) bits[i] = 0u;
+  __syncthreads();
+  const int32_t* c = a.cand + (int64_t)r * a.n_cand;
+  for (int i = threadIdx.x; i < a.n_cand; i += kNT) {
+    const int64_t x = (int64_t)c[i] - g0;
+    if (c[i] >= 0 && x >= 0 && x < ng) atomicOr(&bits[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+}
+
+// Masked kernels: load_keys with the thread's keys (segment positions base .. base +
+// E - 1, keys key_base + position) outside the candidate groups read as -inf; bits
+// start at group g0. With groups of whole quads (key_base and base are multiples of 4)
+// one test covers a 16-byte load.
+template <int E>
+__device__ __forceinline__ void load_keys_masked(const float* seg, int n, bool vec, const TopkArgs& a,
+                                                 int64_t key_base, int64_t g0, const uint32_t* bits,
+                                                 uint32_t (&key)[E]) {
+  const int base = threadIdx.x * E;
+  const int64_t k0 = key_base + base;
+  int grp = (int)(k0 / a.group - g0);
+  int rem = (int)(k0 % a.group);
+  const uint32_t ninf = order_key(-__builtin_inff());
+  if (vec && a.group % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const int i = base + 4 * j;
+      const bool in = (bits[grp >> 5] >> (grp & 31)) & 1u;
+      const float4 v = i < n ? *(const float4*)(seg + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      key[4 * j + 0] = i + 0 < n ? (in ? order_key(v.x) : ninf) : 0u;
+      key[4 * j + 1] = i + 1 < n ? (in ? order_key(v.y) : ninf) : 0u;
+      key[4 * j + 2] = i + 2 < n ? (in ? order_key(v.z) : ninf) : 0u;
+      key[4 * j + 3] = i + 3 < n ? (in ? order_key(v.w) : ninf) : 0u;
+      rem += 4;
+      if (rem == a.group) {
+        rem = 0;
+        ++grp;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool in = (bits[grp >> 5] >> (grp & 31)) & 1u;
+    key[e] = base + e < n ? (in ? order_key(seg[base + e]) : ninf) : 0u;
+    if (++rem == a.group) {
+      rem = 0;
+      ++grp;
+    }
+  }
+}
 
 __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
   int nv = a.n_valid ? a.n_valid[r] : (int)a.ld;
@@ -343,11 +403,10 @@ __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
 template <int E>
 constexpr int kWavesPerSimd = E == 32 ? 8 : 4;
 
-// One workgroup per row.
-template <int E>
-__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_kernel(TopkArgs a) {
-  __shared__ SelShared sh;
-  __shared__ CandShared cs;
+// One workgroup per row. MASK: keys outside the row's candidate groups read as -inf
+// (a consumer's masking folded into the load; the logits are not written).
+template <int E, bool MASK>
+__device__ __forceinline__ void topk_row_body(const TopkArgs& a, SelShared& sh, CandShared& cs, uint32_t* bits) {
   const int r = blockIdx.x;
   const int n = row_valid(a, r);
   int32_t* out = a.blocks + (int64_t)r * a.k;
@@ -355,19 +414,34 @@ __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_kernel(TopkArg
     for (int i = threadIdx.x; i < a.k; i += kNT) out[i] = i < n ? i : -1;
     return;
   }
+  if constexpr (MASK) load_candidates(a, r, 0, (n + a.group - 1) / a.group, bits);
   uint32_t key[E];
-  load_keys<E>(a.logits + (int64_t)r * a.ld, n, a.vec, key);
+  if constexpr (MASK) load_keys_masked<E>(a.logits + (int64_t)r * a.ld, n, a.vec, a, 0, 0, bits, key);
+  else load_keys<E>(a.logits + (int64_t)r * a.ld, n, a.vec, key);
   const int base = threadIdx.x * E;
   select_topk<E>(key, a.k, sh, cs, [&](int e) { return base + e; },
                  [&](uint32_t pos, uint32_t, int32_t i) { out[pos] = i; });
 }
 
-// Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row, in
-// index order, padded with key 0 to kp.
 template <int E>
-__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
+  topk_row_body<E, false>(a, sh, cs, nullptr);
+}
+
+template <int E>
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_masked_kernel(TopkArgs a) {
+  __shared__ SelShared sh;
+  __shared__ CandShared cs;
+  __shared__ uint32_t bits[kMaskWords];
+  topk_row_body<E, true>(a, sh, cs, bits);
+}
+
+// Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row, in
+// index order, padded with key 0 to kp. MASK as for the row kernel.
+template <int E, bool MASK>
+__device__ __forceinline__ void topk_stage1_body(const TopkArgs& a, SelShared& sh, CandShared& cs, uint32_t* bits) {
   const int r = blockIdx.y;
   const int bb = blockIdx.x + a.blk0;
   const int nv = row_valid(a, r);
@@ -379,15 +453,23 @@ __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(Topk
   uint32_t* ck = a.ws_key + ((int64_t)r * a.nblk + bb) * a.kp;
   int32_t* ci = a.ws_idx + ((int64_t)r * a.nblk + bb) * a.kp;
   const float* row = a.logits + (int64_t)r * a.ld + (i0 - a.key0);
+  const int64_t g0 = MASK ? i0 / a.group : 0;
+  if constexpr (MASK) load_candidates(a, r, g0, n > 0 ? (int)((i0 + n - 1) / a.group - g0 + 1) : 0, bits);
   if (n <= a.k) {
     for (int i = threadIdx.x; i < a.kp; i += kNT) {
-      ck[i] = i < n ? order_key(row[i]) : 0u;
+      uint32_t kv = i < n ? order_key(row[i]) : 0u;
+      if constexpr (MASK) {
+        const int64_t gi = (int64_t)(i0 + i) / a.group - g0;
+        if (i < n && !((bits[gi >> 5] >> (gi & 31)) & 1u)) kv = order_key(-__builtin_inff());
+      }
+      ck[i] = kv;
       ci[i] = i < n ? i0 + i : -1;
     }
     return;
   }
   uint32_t key[E];
-  load_keys<E>(row, n, a.vec, key);
+  if constexpr (MASK) load_keys_masked<E>(row, n, a.vec, a, i0, g0, bits, key);
+  else load_keys<E>(row, n, a.vec, key);
   const int base = i0 + threadIdx.x * E;
   for (int i = a.k + threadIdx.x; i < a.kp; i += kNT) {   // padding past k
     ck[i] = 0u;
@@ -397,6 +479,21 @@ __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(Topk
     ck[pos] = kv;
     ci[pos] = i;
   });
+}
+
+template <int E>
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(TopkArgs a) {
+  __shared__ SelShared sh;
+  __shared__ CandShared cs;
+  topk_stage1_body<E, false>(a, sh, cs, nullptr);
+}
+
+template <int E>
+__global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_masked_kernel(TopkArgs a) {
+  __shared__ SelShared sh;
+  __shared__ CandShared cs;
+  __shared__ uint32_t bits[kMaskWords];
+  topk_stage1_body<E, true>(a, sh, cs, bits);
 }
 
 // Blocked mode, stage 2: merge the candidates of all key blocks of one row (they are in
@@ -464,12 +561,14 @@ size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k) {
 
 template <int E>
 static void launch_row(const TopkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(topk_row_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
+  if (a.cand) hipLaunchKernelGGL(topk_row_masked_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL(topk_row_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
 }
 
 template <int E>
 static void launch_stage1(const TopkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(topk_stage1_kernel<E>, dim3(a.nblk, a.n_rows), dim3(kNT), 0, st, a);
+  if (a.cand) hipLaunchKernelGGL(topk_stage1_masked_kernel<E>, dim3(a.nblk, a.n_rows), dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL(topk_stage1_kernel<E>, dim3(a.nblk, a.n_rows), dim3(kNT), 0, st, a);
 }
 
 template <int E>
@@ -481,7 +580,8 @@ static void launch_stage2(const TopkArgs& a, hipStream_t st) {
 static int run_for(int64_t n) { return n <= 4 * kNT ? 4 : (n <= 8 * kNT ? 8 : (n <= 16 * kNT ? 16 : 32)); }
 
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid, int32_t k,
-                      int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st) {
+                      int32_t* blocks, void* ws, size_t ws_bytes, hipStream_t st, const int32_t* cand,
+                      int32_t n_cand, int32_t group) {
   (void)ws_bytes;
   TopkArgs a;
   a.logits = logits;
@@ -489,6 +589,9 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   a.ncap = ld;
   a.blk0 = 0;
   a.key0 = 0;
+  a.cand = cand;
+  a.n_cand = n_cand;
+  a.group = group;
   a.n_rows = n_rows;
   a.n_valid = n_valid;
   a.k = k;
@@ -559,6 +662,9 @@ static TopkArgs block_args(const float* logits_blk, int32_t B, int32_t nb, int64
   a.ws_idx = (int32_t*)((char*)cand + (size_t)n_rows * nb * a.kp * 4);
   a.blk0 = 0;
   a.key0 = 0;
+  a.cand = nullptr;
+  a.n_cand = 0;
+  a.group = 1;
   return a;
 }
 

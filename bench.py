@@ -448,19 +448,16 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
 def bench_candidates(tf, logits, nv, k, reps, hbm, group=8, n_cand=2048):
     """Two-level selection on the chunk's logits: the candidate layer's top-2,048 groups
     of 8 keys (tf_candidate_groups: reads the logits, writes the group maxima, selects),
-    then a consumer's top-512 inside them (tf_topk_in_candidates on a copy: masks the
-    non-candidates in place, selects). The consumer is timed on the same copy again
-    and again: masking writes the same -inf quads each time. Algorithmic bytes: the
-    logits read and the group maxima written; the -inf quads written and the logits
-    read."""
+    then a consumer's top-512 inside them (tf_topk_in_candidates: the top-k with the
+    non-candidates read as -inf). Algorithmic bytes: the logits read and the group
+    maxima written; the logits and the candidate lists read."""
     import numpy as np
     import torch
     T, ld = logits.shape
     cand = torch.empty((T, n_cand), dtype=torch.int32, device="cuda")
     f1 = tf.candidate_groups(logits, nv, group, n_cand, cand, prepare=True)
-    work = logits.clone()
     blk = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    f2 = tf.topk_in_candidates(work, nv, cand, group, k, blk, prepare=True)
+    f2 = tf.topk_in_candidates(logits, nv, cand, group, k, blk, prepare=True)
     f1()
     f2()
     torch.cuda.synchronize()
@@ -475,10 +472,8 @@ def bench_candidates(tf, logits, nv, k, reps, hbm, group=8, n_cand=2048):
         res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
     nvh = nv.cpu().numpy().astype(np.int64)
     n_groups = (nvh + group - 1) // group
-    masked_keys = int(np.maximum(0, nvh - group * np.minimum(n_groups, n_cand)).sum())
     b1 = int(nvh.sum()) * 4 + int(n_groups.sum()) * 4
-    b2 = masked_keys * 4 + int(nvh.sum()) * 4
-    del work
+    b2 = int(nvh.sum()) * 4 + int(nvh.size) * n_cand * 4
     return {"group": group, "n_cand": n_cand, "k": k,
             "candidate_groups": {"us": round(res["candidate_groups"], 2), "alg_bytes": b1,
                                  "roofline": hbm(b1, res["candidate_groups"])},

@@ -240,18 +240,17 @@ size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, in
  * ws: 16-byte aligned device workspace of at least
  * tf_candidate_groups_workspace_bytes(n_rows, ld, group, n_cand) bytes.
  *
- * tf_topk_in_candidates: the consumer. The visible keys of row r outside its
- * candidate groups (cand [n_rows][n_cand], entries < 0 ignored) are set to
- * -inf IN PLACE in logits, as the pages' masked_fill_ does, and blocks receives
- * the row's top-k as tf_topk_blocks selects it from the masked row (fewer than
- * k candidate keys: the lowest-index others complete it). Keys at or past
- * n_valid are not touched. At most 262,144 groups a row. ws: as for
- * tf_topk_blocks (tf_topk_in_candidates_workspace_bytes). */
+ * tf_topk_in_candidates: the consumer. blocks receives row r's top-k as
+ * tf_topk_blocks selects it from the row with its visible keys outside its
+ * candidate groups (cand [n_rows][n_cand], entries < 0 ignored) read as -inf,
+ * the pages' masked_fill_ (fewer than k candidate keys: the lowest-index others
+ * complete it). The masking happens as the keys are loaded: logits are read
+ * only. ws: as for tf_topk_blocks (tf_topk_in_candidates_workspace_bytes). */
 tf_status tf_candidate_groups(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                               int32_t group, int32_t n_cand, int32_t* cand, void* ws, size_t ws_bytes,
                               void* stream);
 size_t tf_candidate_groups_workspace_bytes(int32_t n_rows, int64_t ld, int32_t group, int32_t n_cand);
-tf_status tf_topk_in_candidates(float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
+tf_status tf_topk_in_candidates(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,
                                 const int32_t* cand, int32_t n_cand, int32_t group, int32_t k,
                                 int32_t* blocks, void* ws, size_t ws_bytes, void* stream);
 size_t tf_topk_in_candidates_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k);

@@ -625,7 +625,9 @@ def test_candidate_selection_against_oracle(group, n_cand, k):
     """Groups of 8 (quads), 3 (no quads) and 1 (plain top-k), ragged rows whose last group
     is partial, a row before the stream's start, tied values; consumers with more
     candidate keys than k and with fewer (n_cand 5 x 8 keys < 64: completed by the
-    lowest-index others). Exact against the oracle on the same fp32 values."""
+    lowest-index others); one workgroup per row (3,000 or 20,000 keys) and, on a few
+    long rows, the per-block kernels. Exact against the oracle on the same fp32
+    values."""
     from oracle import candidate_groups as o_cand, topk_in_candidates as o_topk
     _log(f"candidate selection: groups of {group}, {n_cand} candidates, top-{k}")
     rng = np.random.default_rng(group * 1000 + n_cand)
@@ -642,16 +644,32 @@ def test_candidate_selection_against_oracle(group, n_cand, k):
     lg2 = lg.clone()
     tf.topk_in_candidates(lg2, nvt, cand, group, k, blk)
     torch.cuda.synchronize()
-    assert torch.equal(lg, torch.from_numpy(v).cuda())        # the candidate call only reads
+    assert torch.equal(lg, torch.from_numpy(v).cuda())        # both calls only read the logits
+    assert torch.equal(lg2, lg)
     ref_c = o_cand(v, nv, group, n_cand)
     assert np.array_equal(host(cand), ref_c)
     assert np.array_equal(host(blk), o_topk(v, nv, ref_c, group, k))
-    # masked in place: visible non-candidates are -inf, the rest unchanged
-    m = host(lg2)
-    for r in (0, 1, 4, 5):
-        keep = np.zeros(ld, dtype=bool)
-        for c in ref_c[r][ref_c[r] >= 0]:
-            keep[c * group:(c + 1) * group] = True
-        vis = np.arange(ld) < nv[r]
-        assert np.all(m[r][vis & ~keep] == -np.inf)
-        assert np.array_equal(m[r][~(vis & ~keep)], v[r][~(vis & ~keep)])
+
+
+@pytest.mark.parametrize("group,n_cand,k", [(8, 2048, 512), (3, 700, 300)])
+def test_candidate_selection_long_rows(group, n_cand, k):
+    """A few long rows (40,000 keys): the consumer's top-k runs per key block (masked
+    stage 1, then the merge), and groups straddle the blocks when the group does not
+    divide them (groups of 3)."""
+    from oracle import candidate_groups as o_cand, topk_in_candidates as o_topk
+    _log(f"candidate selection on long rows: groups of {group}, {n_cand} candidates, top-{k}")
+    rng = np.random.default_rng(group + n_cand)
+    R, ld = 6, 40000
+    v = rng.standard_normal((R, ld)).astype(np.float32)
+    v[1] = np.round(v[1], 1)
+    nv = np.array([ld, ld - 5, 33000, 4097, 9000, 12], dtype=np.int32)
+    lg = torch.from_numpy(v).cuda()
+    nvt = torch.from_numpy(nv).cuda()
+    cand = torch.empty((R, n_cand), dtype=torch.int32, device="cuda")
+    tf.candidate_groups(lg, nvt, group, n_cand, cand)
+    blk = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    tf.topk_in_candidates(lg, nvt, cand, group, k, blk)
+    torch.cuda.synchronize()
+    ref_c = o_cand(v, nv, group, n_cand)
+    assert np.array_equal(host(cand), ref_c)
+    assert np.array_equal(host(blk), o_topk(v, nv, ref_c, group, k))
