@@ -121,39 +121,25 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
       for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
     }
   };
-  // three subtiles in flight: slot s holds subtile kb + 32 (3i + s); a range of one
-  // whole page loads its four subtiles at once
-  auto step = [&](int64_t kt, bf16x8 (&cur)[KS], bool refill) {
+  // three subtiles in flight: slot s holds subtile kb + 32 (3i + s)
+  auto step = [&](int64_t kt, bf16x8 (&cur)[KS]) {
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], cur[ks], acc, 0, 0, 0);
     const int pg = page_at(kt);
-    if (refill && kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
+    if (kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
     const float s = weighted_relu_sum<H>(wv, acc, 0);
     const int64_t key = kt + n;
     if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
   };
   bf16x8 s0[KS], s1[KS], s2[KS];
-  if (kend - kb == kKeysPerPage) {
-    // a whole page (the decode case): all four subtiles' loads in flight at once
-    bf16x8 s3[KS];
-    load(kb, s0);
-    load(kb + 32, s1);
-    load(kb + 64, s2);
-    load(kb + 96, s3);
-    step(kb, s0, false);
-    step(kb + 32, s1, false);
-    step(kb + 64, s2, false);
-    step(kb + 96, s3, false);
-  } else {
-    if (kb < kend) load(kb, s0);
-    if (kb + 32 < kend) load(kb + 32, s1);
-    if (kb + 64 < kend) load(kb + 64, s2);
-    for (int64_t kt = kb; kt < kend; kt += 96) {
-      step(kt, s0, true);
-      if (kt + 32 < kend) step(kt + 32, s1, true);
-      if (kt + 64 < kend) step(kt + 64, s2, true);
-    }
+  if (kb < kend) load(kb, s0);
+  if (kb + 32 < kend) load(kb + 32, s1);
+  if (kb + 64 < kend) load(kb + 64, s2);
+  for (int64_t kt = kb; kt < kend; kt += 96) {
+    step(kt, s0);
+    if (kt + 32 < kend) step(kt + 32, s1);
+    if (kt + 64 < kend) step(kt + 64, s2);
   }
   // keys past the compressed length
   for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) out[key] = ninf;
