@@ -295,3 +295,87 @@ def test_indexer_topk_blocked_chunk_full():
     _log(f"blocked indexer + top-k: oracle on {len(sample)} sampled rows")
     ref_l = ow.logits(wl, 0, srows, ld)
     check_topk_against_oracle(host(got)[sample], ref_l, host(nv)[sample], k)
+
+
+def test_decode_step_graph_replays():
+    """The whole decode step (write, indexer, top-k, attention over 8 x 131,072 tokens)
+    captured as one HIP graph: replays with three different input sets copied in
+    between, and eager steps between replays, each replay equal bit for bit to the
+    eager step on the same inputs. No call of the step records a memset or allocates."""
+    from synth import TAG_LATENT, TAG_PKEY
+    from synth.configs import LAT, ROPE, ROW
+    from synth.device import _rid, fill_bf16
+    wl = decode_batch(0)
+    _log("decode graph: populating")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    view = P.view()
+    R, ld, scale = 8, 32768, 1.0 / math.sqrt(576.0)
+    sets = []
+    for back in (1, 2, 3):                                  # rows at L-1, L-2, L-3
+        rows = [(b, wl.lengths[b] - back) for b in range(R)]
+        rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+        lat = torch.empty((R, LAT), dtype=torch.bfloat16, device="cuda")
+        rope = torch.empty((R, ROPE), dtype=torch.bfloat16, device="cuda")
+        key = torch.empty((R, wl.Dk), dtype=torch.bfloat16, device="cuda")
+        for i, (b, t) in enumerate(rows):
+            r0 = _rid(0, b, t)
+            fill_bf16(lat[i:], 1, LAT, wl.seed, TAG_LATENT, r0 * ROW, ROW, ROW)
+            fill_bf16(rope[i:], 1, ROPE, wl.seed, TAG_LATENT, r0 * ROW + LAT, ROW, ROW)
+            fill_bf16(key[i:], 1, wl.Dk, wl.seed, TAG_PKEY, _rid(0, b, t // 4) * wl.Dk, wl.Dk, wl.Dk)
+        kidx = torch.tensor([t // 4 for _, t in rows], dtype=torch.int32, device="cuda")
+        sets.append((rs, rp, iq, w, q, lat, rope, key, kidx))
+    # the step's tensors: inputs copied in from a set, outputs read after each run
+    cur = [x.clone() for x in sets[0]]
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    blocks = torch.empty((R, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+    tws = torch.empty(max(1, tf.topk_workspace_bytes(R, ld, wl.k)), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(max(1, tf.attn_workspace_bytes(R, wl.Hq, wl.k)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rs, rp, iq, w, q, lat, rope, key, kidx = cur
+        tf.latent_write(plan, view, rs, rp, lat, rope, pkey_stream=rs, pkey_idx=kidx, pkeys=key)
+        tf.indexer_logits(plan, view, rs, rp, iq, w, logits, n_valid=nv)
+        tf.topk_blocks(logits, nv, wl.k, blocks, ws=tws)
+        tf.sparse_mla_attn(plan, view, rs, rp, q, scale, blocks, out, lse, ws=aws)
+
+    def load(i):
+        for dst, src in zip(cur, sets[i]):
+            dst.copy_(src)
+
+    def results():
+        torch.cuda.synchronize()
+        return [x.clone() for x in (logits, nv, blocks, out, lse)]
+
+    want = []
+    for i in range(3):
+        load(i)
+        step()
+        want.append(results())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for n in range(9):
+        i = n % 3
+        load(i)
+        out.fill_(7.0)
+        blocks.fill_(-7)
+        g.replay()
+        got = results()
+        _log(f"decode graph: replay {n} (inputs {i})")
+        for a, b in zip(got, want[i]):
+            assert torch.equal(a, b), f"replay {n}"
+        if n % 2 == 1:                                      # eager work between replays
+            load((i + 1) % 3)
+            step()
+            for a, b in zip(results(), want[(i + 1) % 3]):
+                assert torch.equal(a, b), f"eager after replay {n}"
