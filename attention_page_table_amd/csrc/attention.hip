@@ -852,12 +852,19 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   {
     f32x4 acc[2] = {};
     const int tok = row0 + (lane & 15);
+    // every LDS read of S issued before the first MFMA, held there by a scheduling
+    // barrier (left to itself the scheduler keeps two k-steps in flight, and the chain
+    // waits on LDS latency at every step)
+    bf16x8 aq[18], bk[16];
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const bf16x8 aq = *(const bf16x8*)&sh.qp.q[ks][lane >> 4][lane & 15][0];
-      const bf16x8 bk = ks < 16 ? *(const bf16x8*)&sh.lat[tok][ks * 32 + (lane >> 4) * 8] : br[ks - 16];
-      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, acc[ks & 1], 0, 0, 0);
+      aq[ks] = *(const bf16x8*)&sh.qp.q[ks][lane >> 4][lane & 15][0];
+      if (ks < 16) bk[ks] = *(const bf16x8*)&sh.lat[tok][ks * 32 + (lane >> 4) * 8];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks)
+      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], ks < 16 ? bk[ks] : br[ks - 16], acc[ks & 1], 0, 0, 0);
     const bool att = (vmask >> (lane & 15)) & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
