@@ -875,12 +875,17 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();   // every wave's maxima; every wave is past its reads of the queries
   {
+    // the waves' maxima of this lane's four heads: one 16-byte read per wave, all
+    // issued before the first is used
+    float4 wm[kDecWaves];
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) wm[w] = *(const float4*)&sh.wmax[w][4 * (lane >> 4)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * (lane >> 4) + i;
-      float m = sh.wmax[0][h];
+      float m = wm[0][i];
 #pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) m = __builtin_fmaxf(m, sh.wmax[w][h]);
+      for (int w = 1; w < kDecWaves; ++w) m = __builtin_fmaxf(m, wm[w][i]);
       const float p = z[i] == -__builtin_inff() ? 0.f : exp2f(z[i] - m);
       const float ps = group_sum<16>(p);
       if ((lane & 15) == 0) sh.wsum[wave][h] = ps;
@@ -905,22 +910,31 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
   }
   // ---- O = P V: wave w owns columns 64w .. 64w + 63 (4 tiles of 16) ---------------------
   constexpr int kNTd = 4;
-  const int ntok = (j1 > j0 ? j1 - j0 : 0) * kPoolRatio;
-  const int nks = (ntok + 31) / 32;   // k-steps of 32 tokens holding any selected token
+  // All four k-steps of 32 tokens run, whatever the split holds: a token it does not
+  // attend has P = 0 and a zeroed row, so its products are exact zeros. Every LDS read
+  // is issued before the first MFMA (held there by a scheduling barrier).
+  constexpr int kKsd = kDecTok / 32;
   F::acc_t o[kNTd];
 #pragma unroll
   for (int nt = 0; nt < kNTd; ++nt) o[nt] = F::acc_t{};
   {
     const int arow = lane & 15, grp = lane >> 4, j = lane & 15;
-    for (int ks = 0; ks < nks; ++ks) {
-      const bf16x8 ph = *(const bf16x8*)&sh.qp.p.hi[arow][ks * 32 + grp * 8];
-      const bf16x8 pl = *(const bf16x8*)&sh.qp.p.lo[arow][ks * 32 + grp * 8];
+    bf16x8 ph[kKsd], pl[kKsd], vb[kKsd][kNTd];
 #pragma unroll
-      for (int nt = 0; nt < kNTd; ++nt) {
-        const bf16x8 vb = bfrag_tr(&sh.lat[0][0], kDecRS, ks * 32 + grp * 8, wave * 64 + nt * 16, j);
-        o[nt] = F::mfma(ph, vb, o[nt]);
-        o[nt] = F::mfma(pl, vb, o[nt]);
-      }
+    for (int ks = 0; ks < kKsd; ++ks) {
+      ph[ks] = *(const bf16x8*)&sh.qp.p.hi[arow][ks * 32 + grp * 8];
+      pl[ks] = *(const bf16x8*)&sh.qp.p.lo[arow][ks * 32 + grp * 8];
+#pragma unroll
+      for (int nt = 0; nt < kNTd; ++nt)
+        vb[ks][nt] = bfrag_tr(&sh.lat[0][0], kDecRS, ks * 32 + grp * 8, wave * 64 + nt * 16, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < kKsd; ++ks) {
+#pragma unroll
+      for (int nt = 0; nt < kNTd; ++nt) o[nt] = F::mfma(ph[ks], vb[ks][nt], o[nt]);
+#pragma unroll
+      for (int nt = 0; nt < kNTd; ++nt) o[nt] = F::mfma(pl[ks], vb[ks][nt], o[nt]);
     }
   }
   __syncthreads();   // l_run, bad
