@@ -27,7 +27,7 @@ Reported:
 * the dense pass (no indexer or top-k) over a 2,048-row chunk at L = 4,096;
 * the oracle timed on the host cores on a bounded sample of the same step.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 500] [--warmup 20]
 
 Profile summaries (no GPU needed; reads rocprofv3's SQLite output):
     python bench.py --summarize-trace DB --label NAME --command "..."
@@ -137,13 +137,13 @@ def load_traffic(entry):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=6, help="pool copies rotated between steps")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed passes of the whole prefill-chunk step")
     ap.add_argument("--dense-reps", type=int, default=10, help="timed calls of the dense pass")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the dominant call with events on every n-th timed step")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length")
