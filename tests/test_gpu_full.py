@@ -379,3 +379,37 @@ def test_decode_step_graph_replays():
             step()
             for a, b in zip(results(), want[(i + 1) % 3]):
                 assert torch.equal(a, b), f"eager after replay {n}"
+
+
+def test_candidate_selection_chunk_full():
+    """Two-level selection on the prefill chunk's own logits (2,048 rows x 25,000 keys,
+    as the bench times it): top-2,048 groups of 8 keys, then top-512 inside them;
+    sampled rows exact against the oracle on the same fp32 values, and the logits
+    left unchanged."""
+    from oracle import candidate_groups as o_cand, topk_in_candidates as o_topk
+    wl = prefill_chunk(0)
+    _log("candidate selection, full chunk: populating")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows, ld = wl.rows, 25000
+    R = len(rows)
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, P.view(), rs, rp, iq, w, logits, n_valid=nv)
+    before = logits.clone()
+    cand = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
+    tf.candidate_groups(logits, nv, 8, 2048, cand)
+    blk = torch.empty((R, wl.k), dtype=torch.int32, device="cuda")
+    tf.topk_in_candidates(logits, nv, cand, 8, wl.k, blk)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, before)
+    rng = np.random.default_rng(11)
+    sample = sorted(set([0, 2047] + rng.choice(2048, 10, replace=False).tolist()))
+    _log(f"candidate selection, full chunk: oracle on {len(sample)} sampled rows")
+    lg = host(logits)[sample]
+    nvs = host(nv)[sample]
+    ref_c = o_cand(lg, nvs, 8, 2048)
+    assert np.array_equal(host(cand)[sample], ref_c)
+    assert np.array_equal(host(blk)[sample], o_topk(lg, nvs, ref_c, 8, wl.k))
