@@ -63,7 +63,7 @@ ENTRIES = {
     "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
     "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, false>",), "indexer.hip"),
     "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4>"), "topk.hip"),
-    "topk_prefill": (("tf::topk_row_kernel<32>",), "topk.hip"),
+    "topk_prefill": (("tf::topk_row_kernel<28>",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
     "attention_prefill": (("tf::attn_kernel",), "attention.hip"),
     "attention_dense": (("tf::attn_dense_kernel_w32",), "attention.hip"),
