@@ -401,7 +401,7 @@ __device__ __forceinline__ int row_valid(const TopkArgs& a, int r) {
 // 1,024 threads per CU (8 waves per SIMD, at most 64 VGPRs) where the LDS allows it,
 // so that one workgroup's loads overlap the other's selection.
 template <int E>
-constexpr int kWavesPerSimd = E >= 28 ? 8 : 4;
+constexpr int kWavesPerSimd = E >= 24 ? 8 : 4;
 
 // One workgroup per row. MASK: keys outside the row's candidate groups read as -inf
 // (a consumer's masking folded into the load; the logits are not written).
@@ -576,12 +576,13 @@ static void launch_stage2(const TopkArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(topk_stage2_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
 }
 
-// Smallest per-thread run E in {4, 8, 16, 28, 32} that covers n keys. 28 keys a thread
-// (rows of up to 28,672 keys) fit 63 VGPRs with no spill, where 32 spill 16 bytes a
-// lane at the 64-VGPR bound of two workgroups per CU; only the row kernel takes 28
-// (the per-block kernels run 32).
+// Smallest per-thread run E in {4, 8, 16, 24, 28, 32} that covers n keys. 24 and 28
+// keys a thread (rows of up to 28,672 keys) fit 64 VGPRs with no spill, where 32 spill
+// 16 bytes a lane at the 64-VGPR bound of two workgroups per CU; only the row kernel
+// takes 24 and 28 (the per-block kernels run 32).
 static int run_for(int64_t n) {
-  return n <= 4 * kNT ? 4 : (n <= 8 * kNT ? 8 : (n <= 16 * kNT ? 16 : (n <= 28 * kNT ? 28 : 32)));
+  return n <= 4 * kNT ? 4
+                      : (n <= 8 * kNT ? 8 : (n <= 16 * kNT ? 16 : (n <= 24 * kNT ? 24 : (n <= 28 * kNT ? 28 : 32))));
 }
 
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid, int32_t k,
@@ -613,6 +614,7 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
       case 4: launch_row<4>(a, st); break;
       case 8: launch_row<8>(a, st); break;
       case 16: launch_row<16>(a, st); break;
+      case 24: launch_row<24>(a, st); break;
       case 28: launch_row<28>(a, st); break;
       default: launch_row<32>(a, st); break;
     }

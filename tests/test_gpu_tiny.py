@@ -251,14 +251,15 @@ def test_topk_sampled_threshold_paths():
     """Rows of 16 and 32 keys per thread cut their keys down with a threshold from
     per-group maxima (1, 2 or 4 samples per thread as k grows) before the exact
     selection; ragged rows, few visible samples, heavy ties (the whole-row fallback)
-    and continuous values all give the exact top-k. Rows of 8 keys per thread (up to
-    8,192 keys) select on the whole row."""
+    and continuous values all give the exact top-k; rows of 24 and 28 keys per thread
+    (16,385 .. 28,672 keys) included. Rows of 8 keys per thread (up to 8,192 keys)
+    select on the whole row."""
     _log("top-k: sampled thresholds, k up to 2048, fallbacks")
     rng = np.random.default_rng(13)
     for ld, k, ties in [(20000, 512, False), (20000, 1000, False), (30000, 1500, False), (32768, 2048, False),
                         (10000, 700, False), (20000, 512, True), (32768, 2048, True),
                         (8192, 512, False), (6000, 1000, False), (8000, 2000, False), (8192, 2048, False),
-                        (8192, 512, True)]:
+                        (8192, 512, True), (24576, 2048, False), (25000, 512, False), (28672, 1500, True)]:
         R = 130                                                    # >= 128 rows: one workgroup per row
         v = rng.standard_normal((R, ld)).astype(np.float32)
         if ties:
