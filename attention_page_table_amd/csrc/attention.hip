@@ -45,7 +45,7 @@ namespace tf {
 
 constexpr int kTileTok = 32;
 constexpr int kRS = kRow + 8;       // LDS row stride in bf16 (1,168 bytes)
-constexpr int kMaxWgTok = 2048;     // tokens one workgroup may own (k <= 512 blocks)
+constexpr int kMaxWgTok = 4096;     // tokens one workgroup may own (k <= 1,024 blocks)
 constexpr int kMasked = -1;         // token table: not attended
 constexpr int kUnreadable = -2;     // token table: selected but the table names no page
 
