@@ -577,7 +577,7 @@ def bench_dense(tf, reps):
     flop = tokens * 4 * dw.Hq * 576
     a = flop / (us * 1e-6) / 1e12
     del P
-    return {"call": "tf_dense_mla_attn", "launches": list(ENTRIES["attention_dense"][0]) + ["tf::attn_merge_kernel"],
+    return {"call": "tf_dense_mla_attn", "launches": list(ENTRIES["attention_dense"][0]),
             "workload": f"dense_{R}_at_{dw.lengths[0]}", "rows": R, "n_blocks": nb, "attn_heads": dw.Hq,
             "us": round(us, 2), "reps": reps, "attended_tokens": tokens, "flop": flop,
             "gathered_bytes": tokens * ROW_BYTES,

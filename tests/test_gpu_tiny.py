@@ -491,11 +491,12 @@ DENSE_ROWS = {
 
 @pytest.mark.parametrize("hq", [8, 32])
 @pytest.mark.parametrize("kind", ["decode", "chunk"])
-@pytest.mark.parametrize("n_blocks", [512, 300, 1024])
+@pytest.mark.parametrize("n_blocks", [512, 300, 1024, 2048])
 def test_dense_against_oracle(tiny_pool, hq, kind, n_blocks):
     """Every visible token within the first n_blocks blocks: 512 covers each row's
-    causal range exactly, 300 cuts the later rows at token 1,199, 1024 runs past the
-    streams (two splits for the chunk, the second all masked)."""
+    causal range exactly, 300 cuts the later rows at token 1,199, 1024 and 2048 run
+    past the streams (2048: two 4,096-token splits for the chunk, the second all
+    masked, merged)."""
     _log(f"dense pass: {kind} rows, {hq} heads, n_blocks {n_blocks} (tiny)")
     wl, plan, P = tiny_pool
     wl = _with_heads(wl, hq)
