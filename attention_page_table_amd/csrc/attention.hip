@@ -1058,7 +1058,7 @@ struct SplitPlan {
 
 // Few rows (decode): 16 heads and at most 128 tokens per workgroup, so a row is
 // spread over many CUs. Many rows (prefill): all 32 heads and the whole block list
-// (up to 2,048 tokens) per workgroup.
+// (up to 4,096 tokens) per workgroup.
 static SplitPlan pick_split(int32_t n_rows, int32_t n_heads, int32_t k, bool fp8) {
   SplitPlan p;
   const int tiles = (k + 7) / 8;
