@@ -50,6 +50,7 @@ class tf_kv_view(ctypes.Structure):
 
 # name -> (restype, argtypes), in the order of include/tf.h
 SIGNATURES = {
+    "tf_check_page_table": (_c_i32, [_vp, _c_i32, _c_i32, _c_i32]),
     "tf_kv_pool_plan": (_c_i32, [ctypes.POINTER(tf_geom), ctypes.POINTER(tf_budget), ctypes.POINTER(tf_plan)]),
     "tf_prefill_chunk": (_c_i64, [_c_i64, _c_i64]),
     "tf_latent_write": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i32,
@@ -162,9 +163,22 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def view(pool, pt, pt_stride: int, n_pages: int, cache: int = 0, n_streams: int | None = None) -> tf_kv_view:
+def check_page_table(pt_host, n_pages: int) -> None:
+    """Refuse a host page table [streams, pt_stride] (numpy or CPU tensor, int32) that names a
+    page outside [0, n_pages) (entries of -1 mean no page); raises TFError (TF_E_RANGE)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(pt_host), dtype=np.int32)
+    assert a.ndim == 2, "page table must be [streams, pt_stride]"
+    _check(lib().tf_check_page_table(a.ctypes.data, a.shape[0], a.shape[1], int(n_pages)))
+
+
+def view(pool, pt, pt_stride: int, n_pages: int, cache: int = 0, n_streams: int | None = None,
+         pt_host=None) -> tf_kv_view:
     """pool: uint8 device tensor of n_pages * page_bytes; pt: int32 [streams, pt_stride] or None
-    (then stream b's page i is pool page b * pt_stride + i)."""
+    (then stream b's page i is pool page b * pt_stride + i). pt_host: a host copy of pt, checked
+    with tf_check_page_table before the view is made."""
+    if pt_host is not None:
+        check_page_table(pt_host, n_pages)
     if pt is not None:
         import torch
         assert pt.dtype == torch.int32 and pt.dim() == 2 and pt.shape[1] == pt_stride
@@ -173,7 +187,9 @@ def view(pool, pt, pt_stride: int, n_pages: int, cache: int = 0, n_streams: int 
         ns = max(1, n_pages // pt_stride)
     if n_streams is not None:
         ns = n_streams
-    return tf_kv_view(_ptr(pool), _ptr(pt), pt_stride, ns, n_pages, cache)
+    v = tf_kv_view(_ptr(pool), _ptr(pt), pt_stride, ns, n_pages, cache)
+    v._keep = (pool, pt)   # the view holds raw pointers: keep the tensors alive while it lives
+    return v
 
 
 def latent_write(plan, dst, row_stream, row_pos, latent, rope, row_scale=None,

@@ -68,6 +68,25 @@ using namespace tf;
 
 extern "C" const char* tf_last_error(void) { return g_err; }
 
+extern "C" tf_status tf_check_page_table(const int32_t* pt_host, int32_t n_streams, int32_t pt_stride,
+                                         int32_t n_pages) {
+  clear_error();
+  if (!pt_host) return set_error(TF_E_INVAL, "tf_check_page_table: pt_host must not be NULL");
+  if (n_streams < 1 || pt_stride < 1 || n_pages < 1)
+    return set_error(TF_E_INVAL, "tf_check_page_table: n_streams=%d, pt_stride=%d, n_pages=%d must be >= 1",
+                     n_streams, pt_stride, n_pages);
+  for (int64_t b = 0; b < n_streams; ++b)
+    for (int64_t i = 0; i < pt_stride; ++i) {
+      const int32_t p = pt_host[b * pt_stride + i];
+      if (p < -1 || p >= n_pages)
+        return set_error(TF_E_RANGE,
+                         "tf_check_page_table: stream %lld page index %lld names page %d, outside the pool's "
+                         "[0, %d) (use -1 for no page)",
+                         (long long)b, (long long)i, p, n_pages);
+    }
+  return TF_OK;
+}
+
 extern "C" tf_status tf_latent_write(const tf_plan* p, tf_kv_view dst, int32_t n_rows,
                                      const int32_t* row_stream, const int32_t* row_pos,
                                      const void* latent, const float* row_scale, const void* rope,
@@ -331,27 +350,36 @@ extern "C" size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32
   return attn_ws_bytes(n_rows, n_heads, k);
 }
 
+// Arguments of the sparse pass, checked before any launch (shared by its two entry points).
+static tf_status check_sparse_attn(const char* fn, const tf_plan* p, const tf_kv_view& kv, int32_t n_rows,
+                                   const int32_t* row_stream, const int32_t* row_pos, const void* q,
+                                   int32_t n_heads, float softmax_scale, const int32_t* blocks, int32_t k,
+                                   const float* out) {
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, kv, "kv")) != TF_OK) return s;
+  if (p->g.rope_dim != kRope) return set_error(TF_E_UNSUPPORTED, "%s: needs the 64-value rope plane", fn);
+  if (n_rows < 0) return set_error(TF_E_INVAL, "%s: n_rows < 0", fn);
+  if (n_heads < 1 || n_heads > 32) return set_error(TF_E_UNSUPPORTED, "%s: n_heads=%d, built for 1..32", fn, n_heads);
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "%s: k=%d, need 1..2048", fn, k);
+  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f)
+    return set_error(TF_E_INVAL, "%s: softmax_scale must be > 0", fn);
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !blocks || !out)
+    return set_error(TF_E_INVAL, "%s: row_stream, row_pos, q, blocks and out are required", fn);
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "%s: q must be 16-byte aligned", fn);
+  return TF_OK;
+}
+
 extern "C" tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
                                         const int32_t* row_stream, const int32_t* row_pos,
                                         const void* q, int32_t n_heads, float softmax_scale,
                                         const int32_t* blocks, int32_t k, float* out, float* lse,
                                         void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  tf_status s;
-  if ((s = check_plan(p)) != TF_OK) return s;
-  if ((s = check_view(p, kv, "kv")) != TF_OK) return s;
-  if (p->g.rope_dim != kRope)
-    return set_error(TF_E_UNSUPPORTED, "tf_sparse_mla_attn: needs the 64-value rope plane");
-  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_sparse_mla_attn: n_rows < 0");
-  if (n_heads < 1 || n_heads > 32)
-    return set_error(TF_E_UNSUPPORTED, "tf_sparse_mla_attn: n_heads=%d, built for 1..32", n_heads);
-  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_sparse_mla_attn: k=%d, need 1..2048", k);
-  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f)
-    return set_error(TF_E_INVAL, "tf_sparse_mla_attn: softmax_scale must be > 0");
-  if (n_rows == 0) return TF_OK;
-  if (!row_stream || !row_pos || !q || !blocks || !out)
-    return set_error(TF_E_INVAL, "tf_sparse_mla_attn: row_stream, row_pos, q, blocks and out are required");
-  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_sparse_mla_attn: q must be 16-byte aligned");
+  tf_status s = check_sparse_attn("tf_sparse_mla_attn", p, kv, n_rows, row_stream, row_pos, q, n_heads,
+                                  softmax_scale, blocks, k, out);
+  if (s != TF_OK || n_rows == 0) return s;
   const size_t need = attn_ws_bytes(n_rows, n_heads, k);
   if (need > 0 && (!ws || ws_bytes < need))
     return set_error(TF_E_INVAL, "tf_sparse_mla_attn: workspace of %zu bytes needed, got %zu", need, ws_bytes);

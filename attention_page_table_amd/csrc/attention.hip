@@ -45,7 +45,8 @@ namespace tf {
 
 constexpr int kTileTok = 32;
 constexpr int kRS = kRow + 8;       // LDS row stride in bf16 (1,168 bytes)
-constexpr int kMaxWgTok = 4096;     // tokens one workgroup may own (k <= 1,024 blocks)
+constexpr int kMaxWgTok = 4096;     // tokens one workgroup may own (k <= 1,024 blocks); its 16 KiB
+                                    // token table still lets two workgroups share a CU (asserted below)
 constexpr int kMasked = -1;         // token table: not attended
 constexpr int kUnreadable = -2;     // token table: selected but the table names no page
 
@@ -532,6 +533,14 @@ struct alignas(16) AttnSharedW {
   int32_t moved[2];   // by tile parity: some head's max moved in the tile (O needs a rescale)
   int32_t bad;
 };
+
+// Two workgroups of the 32-head kernels share a CU (__launch_bounds__(256, 2)), which
+// LDS allows only while two copies of their shared state fit its 160 KiB; the token
+// table (kMaxWgTok entries) is most of that state. Launch bounds do not count LDS, so
+// a larger struct would silently halve the occupancy.
+static_assert(2 * sizeof(AttnShared<32>) <= 160 * 1024, "two 32-head workgroups must fit one CU's LDS");
+static_assert(2 * sizeof(AttnShared<16>) <= 160 * 1024, "two 16-head workgroups must fit one CU's LDS");
+static_assert(2 * sizeof(AttnSharedW) <= 160 * 1024, "two sliced 32-head workgroups must fit one CU's LDS");
 
 constexpr float kLazy = 8.f;
 

@@ -39,10 +39,12 @@
  *   - Returns TF_OK or an error code. Arguments are validated on the host before
  *     any launch; on error nothing is enqueued and tf_last_error() (thread-local)
  *     names the argument and the fix. A launch failure reports TF_E_DEVICE.
- *   - Page ids and positions live in device memory and cannot be read by the
- *     host: kernels skip (writes) or produce NaN for (reads) any row whose page
- *     id falls outside [0, n_pages) or whose page index falls outside the
- *     table's stride, so a bad table never leads to an out-of-bounds access.
+ *   - Page ids and positions live in device memory, which the calls do not read
+ *     on the host. A caller that holds a host copy of a table refuses a bad one
+ *     before any launch with tf_check_page_table (TF_E_RANGE). On the device,
+ *     kernels skip (writes) or produce NaN for (reads) any row whose page id
+ *     falls outside [0, n_pages) or whose page index falls outside the table's
+ *     stride, so a bad table never leads to an out-of-bounds access.
  *   - Every call is safe to capture in a HIP graph (no memset, no allocation).
  */
 #ifndef TF_H_
@@ -131,6 +133,15 @@ typedef struct {
   int32_t n_pages;      /* pages in the pool */
   int32_t cache;        /* which cache block of each page (0 <= cache < n_caches) */
 } tf_kv_view;
+
+/* Host only. Checks a page table before it is handed to the device [#1142, "GLM
+ * declares a kv_pool.Layout": kernels take a page table; "Proposal": page ids come
+ * from the host's plan]. pt_host is a host array [n_streams][pt_stride] of int32.
+ * Every entry must be a pool page in [0, n_pages) or -1 (no page yet: reads of
+ * such a row give NaN, writes to it are skipped). Returns TF_E_RANGE naming the
+ * first stream, page index and id that break this, TF_E_INVAL for a NULL table
+ * or non-positive sizes, TF_OK otherwise. Reads nothing but pt_host. */
+tf_status tf_check_page_table(const int32_t* pt_host, int32_t n_streams, int32_t pt_stride, int32_t n_pages);
 
 /* Host only. Fills `out` with the page layout of `g` and, when `budget` is not
  * NULL, the page budget in the pages' plan order [#1313, "Why" and "Proposal"].

@@ -83,6 +83,8 @@ class Pool:
 
 
 def alloc_pool(wl, plan, poison=True) -> Pool:
+    import attention_page_table_amd as tf
+    tf.check_page_table(wl.pt, wl.n_pages)   # refuse a table naming pages outside the pool
     pool = torch.empty(wl.n_pages * plan.page_bytes, dtype=torch.uint8, device="cuda")
     if poison:
         pool.view(torch.int16).fill_(NAN16)

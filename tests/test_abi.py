@@ -189,3 +189,28 @@ def test_validation_refuses_before_launch():
     # a successful call clears the message
     assert L.tf_topk_blocks(fake, 100, 0, None, 4, fake, None, 0, None) == tf.TF_OK
     assert L.tf_last_error().decode() == ""
+
+
+def test_page_table_check_refuses_ids_outside_the_pool():
+    """A host copy of a page table is refused before any launch when it names a page
+    outside [0, n_pages); -1 (no page yet) is accepted."""
+    import numpy as np
+    L = tf.lib()
+    pt = np.array([[3, 0, -1, 2], [1, 4, 5, 6]], dtype=np.int32)
+    tf.check_page_table(pt, 7)
+    assert L.tf_last_error().decode() == ""
+    with pytest.raises(tf.TFError) as e:
+        tf.check_page_table(pt, 6)                         # page 6 is past a 6-page pool
+    assert e.value.status == tf.TF_E_RANGE
+    assert "stream 1 page index 3 names page 6" in str(e.value)
+    bad = pt.copy()
+    bad[0, 1] = -2
+    with pytest.raises(tf.TFError) as e:
+        tf.check_page_table(bad, 7)
+    assert e.value.status == tf.TF_E_RANGE and "stream 0 page index 1" in str(e.value)
+    assert L.tf_check_page_table(None, 1, 1, 1) == tf.TF_E_INVAL
+    assert L.tf_check_page_table(pt.ctypes.data, 2, 4, 0) == tf.TF_E_INVAL
+    # the binding's view checks a host copy when one is given
+    with pytest.raises(tf.TFError):
+        tf.view(None, None, 4, 6, pt_host=pt)
+

@@ -508,10 +508,12 @@ def test_dense_against_oracle(tiny_pool, hq, kind, n_blocks):
 
 
 @pytest.mark.parametrize("kind", ["decode", "chunk"])
-@pytest.mark.parametrize("n_blocks", [512, 200])
+@pytest.mark.parametrize("n_blocks", [512, 200, 1024, 2048])
 def test_dense_equals_sparse_on_every_block_bitwise(tiny_pool, kind, n_blocks):
     """The dense pass is the sparse pass with blocks 0 .. n_blocks - 1 selected: same
-    bits (the slots it cuts hold masked tokens only)."""
+    bits (the slots it cuts hold masked tokens only). At 1,024 and 2,048 blocks the
+    sparse pass's workgroups own 4,096-token lists (one split, or two merged) whose
+    tokens past the streams are masked."""
     _log(f"dense == sparse over blocks 0..{n_blocks - 1}, bit for bit ({kind})")
     wl, plan, P = tiny_pool
     wl = _with_heads(wl, 32)
@@ -549,9 +551,13 @@ def test_dense_bits_do_not_depend_on_pages(tiny_pool):
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("hq", [8, 32])
-def test_dense_fp8_rows(hq):
-    _log(f"dense pass over fp8 rows, {hq} heads (tiny)")
+@pytest.mark.parametrize("hq,rows_kind,n_blocks", [(8, "mixed", 512), (32, "mixed", 512),
+                                                  (32, "chunk", 1024), (32, "chunk", 2048)])
+def test_dense_fp8_rows(hq, rows_kind, n_blocks):
+    """fp8 rows through the dense pass. With 32 heads over the 265 chunk rows the
+    32-head fp8 kernel runs; at 1,024 blocks a workgroup owns one 4,096-token list,
+    at 2,048 two splits are merged."""
+    _log(f"dense pass over fp8 rows, {hq} heads, {rows_kind} rows, n_blocks {n_blocks} (tiny)")
     wl = tiny(1)
     wl.fp8 = True
     wl = _with_heads(wl, hq)
@@ -559,10 +565,43 @@ def test_dense_fp8_rows(hq):
     P = alloc_pool(wl, plan)
     populate(P)
     torch.cuda.synchronize()
-    rows = DENSE_ROWS["decode"] + DENSE_ROWS["chunk"][::4]
-    out, lse = run_dense(wl, plan, P.view(), rows, 512, 24.0)
-    ro, rl = ow.dense_attention(wl, 0, rows, 512, 24.0)
+    rows = DENSE_ROWS["decode"] + DENSE_ROWS["chunk"][::4] if rows_kind == "mixed" else DENSE_ROWS["chunk"]
+    out, lse = run_dense(wl, plan, P.view(), rows, n_blocks, 24.0)
+    ro, rl = ow.dense_attention(wl, 0, rows, n_blocks, 24.0)
     check_attention(out, lse, ro, rl, "dense fp8")
+
+
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_sparse_fp8_long_block_lists(k):
+    """The sparse pass over fp8 rows with 1,024 and 2,048 selected blocks on 265 rows and
+    32 heads (the 32-head fp8 kernel, 4,096-token workgroup lists): every visible
+    block of a row is selected, in a shuffled order padded with blocks past the row
+    and -1 entries; against the oracle on the same lists."""
+    _log(f"sparse pass over fp8 rows, k {k}, 265 rows, 32 heads (tiny)")
+    from oracle import sparse_mla
+    wl = tiny(1)
+    wl.fp8 = True
+    wl = _with_heads(wl, 32)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows = DENSE_ROWS["chunk"]
+    R = len(rows)
+    rng = np.random.default_rng(k)
+    blk = np.full((R, k), -1, dtype=np.int32)
+    for r, (_, t) in enumerate(rows):
+        vis = np.arange(t // 4 + 1)
+        extra = np.arange(t // 4 + 1, t // 4 + 1 + (k - vis.size) // 2)   # past the row: masked
+        lst = np.concatenate([vis, extra]).astype(np.int32)
+        rng.shuffle(lst)
+        blk[r, :lst.size] = lst
+    rs, rp, _, _, q = query_inputs(wl, 0, rows)
+    out = torch.empty((R, 32, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, 32), dtype=torch.float32, device="cuda")
+    tf.sparse_mla_attn(plan, P.view(), rs, rp, q, 24.0, torch.from_numpy(blk).cuda(), out, lse)
+    torch.cuda.synchronize()
+    ro, rl = ow.attention(wl, 0, rows, blk, 24.0)
+    check_attention(host(out), host(lse), ro, rl, f"sparse fp8 k={k}")
 
 
 # ---- key-blocked indexer + top-k -----------------------------------------------------
