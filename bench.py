@@ -121,10 +121,10 @@ def source_hash(name):
     return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(entry):
+def load_traffic(entry, traffic_file=TRAFFIC_FILE):
     """HBM bytes per launch of an entry point from the committed counter summary, or
     None when there is none or the kernel source changed since it was taken."""
-    p = os.path.join(PROFILES, TRAFFIC_FILE)
+    p = os.path.join(PROFILES, traffic_file)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -134,21 +134,26 @@ def load_traffic(entry):
     return e.get("hbm_bytes_per_launch")
 
 
+LEGS = ("decode", "prefill", "dense", "c4", "c5", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=6, help="pool copies rotated between steps")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--legs", default=",".join(LEGS), help="comma list of " + ",".join(LEGS))
+    ap.add_argument("--no-prefill", action="store_true", help="same as leaving prefill, dense, c4, c5 out of --legs")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed passes of the whole prefill-chunk step")
     ap.add_argument("--dense-reps", type=int, default=10, help="timed calls of the dense pass")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket the dominant call with events on every n-th timed step")
+    ap.add_argument("--call-steps", type=int, default=100,
+                    help="decode steps whose calls are each bracketed by events (after the timed region)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length")
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--traffic-file", default=TRAFFIC_FILE, help="profiles/ file --summarize-pmc writes")
     ap.add_argument("--label", default="decode_step")
     ap.add_argument("--command", default="")
     ap.add_argument("--bench-json", help="the line an unprofiled run of the same command printed")
@@ -157,25 +162,75 @@ def main():
         summarize_trace(args.summarize_trace, args.label, args.command, args.bench_json)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.command)
+        summarize_pmc(*args.summarize_pmc, args.command, args.traffic_file)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    legs = set(x for x in args.legs.split(",") if x)
+    unknown = legs - set(LEGS)
+    if unknown:
+        print(f"unknown legs {sorted(unknown)}; choose from {','.join(LEGS)}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_prefill:
+        legs -= {"prefill", "dense", "c4", "c5"}
+    if args.no_cpu:
+        legs.discard("cpu")
 
-    import numpy as np
     import torch
 
     import attention_page_table_amd as tf
-    from synth import TAG_LATENT, TAG_PKEY
-    from synth.configs import LAT, ROPE, ROW, decode_batch, prefill_chunk
-    from synth.device import _rid, alloc_pool, fill_bf16, populate, query_inputs
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     tf.lib()  # fails loudly when the HIP library is missing
 
-    # ------------------------------------------------------------------ decode setup
+    line = {"metric": "paged DSA decode: latent GB/s (% HBM peak); prefill chunk indexer % MFMA peak",
+            "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic"}
+    dec = None
+    if "decode" in legs:
+        dec = bench_decode(tf, args)
+        line.update(dec["line"])
+    if "prefill" in legs:
+        line["prefill_indexer"], line["prefill_step"], pcpu = bench_prefill(tf, args, "cpu" in legs)
+        line["cpu_baseline_prefill_chunk"] = pcpu
+    if "dense" in legs:
+        line["dense_pass"] = bench_dense(tf, args.dense_reps)
+    if "c4" in legs:
+        line["shared_prefix_decode_12_caches"] = bench_shared_prefix(tf)
+    if "c5" in legs:
+        line["adaptive_prefill"] = bench_adaptive_prefill(tf)
+    if "cpu" in legs and dec is not None:
+        cpu = cpu_baseline(dec["wl"], dec["rows"], dec["ld"], dec["scale"], args.cpu_seconds, dec["value_bytes"])
+        cpu["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+def _mean(xs):
+    return float(sum(xs) / len(xs))
+
+
+def _median(xs):
+    v = sorted(xs)
+    n = len(v)
+    return float(v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2]))
+
+
+def bench_decode(tf, args):
+    """The decode batch (8 streams x 131,072 tokens): K timed steps of write -> indexer ->
+    top-k -> attention, then `call_steps` more steps with an event between every call,
+    which give each call's duration (mean over those launches, each with the step's
+    other calls around it) and so the dominant call and its roofline."""
+    import numpy as np
+    import torch
+
+    from synth import TAG_LATENT, TAG_PKEY
+    from synth.configs import LAT, ROPE, ROW, decode_batch
+    from synth.device import _rid, alloc_pool, fill_bf16, populate, query_inputs
+
     wl = decode_batch(0)
     plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
     log(f"setup: {wl.name}: pool {wl.n_pages} pages x {plan.page_bytes} B, {args.replicas} copies")
@@ -215,28 +270,9 @@ def main():
             tf.topk_blocks(logits, nv, wl.k, blocks, prepare=True),
             tf.sparse_mla_attn(plan, v, rs, rp, q, scale, blocks, out, lse, prepare=True),
         ])
-
-    # warmup; its last steps time every call (one HIP event between calls) to find the
-    # dominant call, which the timed region then brackets alone
-    W = max(args.warmup, 3)
-    n_probe = min(8, W - 2)   # the first warmup steps load code objects; they are not probed
-    wev = [[TimingEvent() for _ in range(5)] for _ in range(n_probe)]
-    for i in range(W):
-        ls = launches[i % len(launches)]
-        j = i - (W - n_probe)
-        if j >= 0:
-            wev[j][0].record()
-            for c in range(4):
-                ls[c]()
-                wev[j][c + 1].record()
-        else:
-            for f in ls:
-                f()
-    torch.cuda.synchronize()
-    warm_ms = {n: float(np.median([wev[j][c].elapsed_time(wev[j][c + 1]) for j in range(n_probe)]))
-               for c, n in enumerate(names)}
-    dom = max(["indexer", "topk", "attention"], key=lambda n: warm_ms[n])
-    di = names.index(dom)
+    for i in range(max(args.warmup, 3)):
+        for f in launches[i % len(launches)]:
+            f()
     # calibration stream for the HBM byte counters (outside the timed region)
     cal_src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
     cal_dst = torch.empty_like(cal_src)
@@ -246,32 +282,33 @@ def main():
 
     # ------------------------------------------------------------------ timed region: exactly K steps
     K = args.steps
-    # the dominant call is bracketed by events on every `every`-th step: an event pair
-    # costs the step about 3 us, so bracketing every step would understate the step's
-    # throughput; its duration is the mean over the bracketed launches
-    every = max(1, args.event_every)
-    sampled = list(range(0, K, every))
-    evs = {i: [TimingEvent() for _ in range(2)] for i in sampled}
-    t_start = TimingEvent()
-    t_end = TimingEvent()
+    t_start, t_end = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
     for i in range(K):
-        ls = launches[i % len(launches)]
-        for c in range(4):
-            if c == di and i in evs:
-                evs[i][0].record()
-                ls[c]()
-                evs[i][1].record()
-            else:
-                ls[c]()
+        for f in launches[i % len(launches)]:
+            f()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = t_start.elapsed_time(t_end) / K
-    avg_ms = dict(warm_ms)
-    avg_ms[dom] = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]))
+
+    # ------------------------------------------------------------------ per-call durations
+    # `call_steps` further steps, an event between every call: each call's mean over its
+    # launches (launch to launch, so each also holds one dispatch gap)
+    S = max(50, args.call_steps)
+    ev = [[TimingEvent() for _ in range(5)] for _ in range(S)]
+    for i in range(S):
+        ls = launches[i % len(launches)]
+        ev[i][0].record()
+        for c in range(4):
+            ls[c]()
+            ev[i][c + 1].record()
+    torch.cuda.synchronize()
+    per = {n: [ev[i][c].elapsed_time(ev[i][c + 1]) * 1e3 for i in range(S)] for c, n in enumerate(names)}
+    avg_us = {n: _mean(v) for n, v in per.items()}
+    dom = max(["indexer", "topk", "attention"], key=lambda n: avg_us[n])
 
     lat_bytes = R * wl.k * 4 * ROW_BYTES                       # selected latent + rope rows
     key_bytes = R * ld * wl.Dk * 2                             # every visible pooled key (all rows see ld)
@@ -282,80 +319,86 @@ def main():
         "attention": lat_bytes + R * wl.Hq * 576 * 2 + R * wl.Hq * (512 + 1) * 4 + R * wl.k * 4 + R * 8,
     }
     value = (lat_bytes + key_bytes) / (ms_per_step * 1e-3) / 1e9
-    kern = {n: {"us": round(avg_ms[n] * 1e3, 3), "alg_bytes": alg_bytes[n],
-                "GBps": round(alg_bytes[n] / (avg_ms[n] * 1e-3) / 1e9, 1)} for n in names}
-    achieved = alg_bytes[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    kern = {n: {"us": round(avg_us[n], 3), "us_median": round(_median(per[n]), 3), "alg_bytes": alg_bytes[n],
+                "GBps": round(alg_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1)} for n in names}
+    achieved = alg_bytes[dom] / (avg_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
                 "kernel": f"tf_{'sparse_mla_attn' if dom == 'attention' else dom}",
                 "launches": list(ENTRIES[dom][0]), "alg_bytes_per_launch": alg_bytes[dom],
-                "avg_launch_us": round(avg_ms[dom] * 1e3, 2), "timed_launches": len(sampled),
-                "events_every": every}
+                "avg_launch_us": round(avg_us[dom], 2), "timed_launches": S}
+    att_gbs = lat_bytes / (avg_us["attention"] * 1e-6) / 1e9
+    headline = {"call": "tf_sparse_mla_attn", "launches": list(ENTRIES["attention"][0]),
+                "latent_bytes": lat_bytes, "us": round(avg_us["attention"], 2),
+                "latent_GBps": round(att_gbs, 1), "frac_hbm": round(att_gbs / HBM_PEAK_GBS, 4),
+                "timed_launches": S,
+                "note": "selected latent + rope rows gathered (8 rows x 2,048 tokens x 1,152 B) / the call's "
+                        "mean event interval"}
+    indexer_scan = {"call": "tf_indexer_logits", "key_bytes": key_bytes, "us": round(avg_us["indexer"], 2),
+                    "key_GBps": round(key_bytes / (avg_us["indexer"] * 1e-6) / 1e9, 1)}
+    del launches, views, pools, P0
+    torch.cuda.empty_cache()
+    return {"wl": wl, "rows": rows, "ld": ld, "scale": scale, "value_bytes": lat_bytes + key_bytes,
+            "line": {
+                "value": round(value, 1), "ms_per_step": round(ms_per_step, 5),
+                "config": {"workload": wl.name, "streams": R, "context": wl.lengths[0], "caches": 1,
+                           "attn_heads": wl.Hq, "indexer_heads": wl.H, "index_dim": wl.Dk, "topk_blocks": wl.k,
+                           "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": args.replicas,
+                           "value_bytes_per_step": lat_bytes + key_bytes,
+                           "value": "paged-cache bytes one decode step reads (visible pooled keys + selected "
+                                    "latent and rope rows) / time per step",
+                           "launches": "eager, marshalled once",
+                           "kernels_timing": f"mean of {S} launches per call, an event between every call"},
+                "decode_attention_latent": headline,
+                "decode_indexer_keys": indexer_scan,
+                "roofline": roofline,
+                "kernels": kern,
+                "wall_s_timed": round(wall, 4)}}
 
-    # ------------------------------------------------------------------ prefill indexer
-    prefill = prefill_step = dense = None
-    if not args.no_prefill:
-        del launches, views, pools, P0
-        torch.cuda.empty_cache()
-        pw = prefill_chunk(0)
-        pplan = tf.kv_pool_plan(tf.geom(1, pw.Dk))
-        log(f"setup: {pw.name}")
-        PP = alloc_pool(pw, pplan)
-        populate(PP)
-        prs, prp, piq, pww, _ = query_inputs(pw, 0, pw.rows)
-        pld = (pw.rows[-1][1]) // 4 + 1
-        plog = torch.empty((len(pw.rows), pld), dtype=torch.float32, device="cuda")
-        pnv = torch.empty(len(pw.rows), dtype=torch.int32, device="cuda")
-        f = tf.indexer_logits(pplan, PP.view(), prs, prp, piq, pww, plog, n_valid=pnv, prepare=True)
-        for _ in range(3):
-            f()
-        torch.cuda.synchronize()
-        reps = 20
-        pe = [TimingEvent() for _ in range(reps + 1)]
-        pe[0].record()
-        for i in range(reps):
-            f()
-            pe[i + 1].record()
-        torch.cuda.synchronize()
-        us = float(np.mean([pe[i].elapsed_time(pe[i + 1]) for i in range(reps)])) * 1e3
-        flops = sum(2 * pw.H * pw.Dk * (t // 4 + 1) for _, t in pw.rows)
-        tfl = flops / (us * 1e-6) / 1e12
-        prefill = {"call": "tf_indexer_logits", "launches": list(ENTRIES["indexer_prefill"][0]),
-                   "workload": pw.name, "rows": len(pw.rows), "keys": pld, "us": round(us, 2),
-                   "causal_flop": flops,
-                   "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                                "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
-                                "traffic": load_traffic("indexer_prefill")}}
-        prefill_step = bench_prefill_step(tf, pw, pplan, PP, prs, prp, piq, pww, plog, pnv, args.prefill_reps)
-        del PP, plog
-        torch.cuda.empty_cache()
-        dense = bench_dense(tf, args.dense_reps)
 
-    # ------------------------------------------------------------------ oracle on the host
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(wl, rows, ld, scale, args.cpu_seconds, lat_bytes + key_bytes)
+def bench_prefill(tf, args, with_cpu):
+    """The prefill chunk (2,048 rows against 100,000 tokens): the indexer alone against
+    the MFMA roofline, then the whole chunk step call by call; optionally the oracle on
+    a sample of the chunk's rows."""
+    import numpy as np
+    import torch
 
-    line = {
-        "metric": "paged DSA decode: latent GB/s (% HBM peak); prefill chunk indexer % MFMA peak",
-        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "streams": R, "context": wl.lengths[0], "caches": 1,
-                   "attn_heads": wl.Hq, "indexer_heads": wl.H, "index_dim": wl.Dk, "topk_blocks": wl.k,
-                   "page_rows": 512, "pool_pages": wl.n_pages, "pool_copies": args.replicas,
-                   "value_bytes_per_step": lat_bytes + key_bytes,
-                   "launches": "eager, marshalled once; HIP events (no system fence) around the dominant call only",
-                   "kernels_timing": "dominant call: mean over the timed region; the others: median of the last warmup steps"},
-        "roofline": roofline,
-        "kernels": kern,
-        "prefill_indexer": prefill,
-        "prefill_step": prefill_step,
-        "dense_pass": dense,
-        "cpu_baseline": cpu,
-        "wall_s_timed": round(wall, 4),
-    }
-    print(json.dumps(line), flush=True)
+    from synth.configs import prefill_chunk
+    from synth.device import alloc_pool, populate, query_inputs
+    pw = prefill_chunk(0)
+    pplan = tf.kv_pool_plan(tf.geom(1, pw.Dk))
+    log(f"setup: {pw.name}")
+    PP = alloc_pool(pw, pplan)
+    populate(PP)
+    prs, prp, piq, pww, _ = query_inputs(pw, 0, pw.rows)
+    pld = (pw.rows[-1][1]) // 4 + 1
+    plog = torch.empty((len(pw.rows), pld), dtype=torch.float32, device="cuda")
+    pnv = torch.empty(len(pw.rows), dtype=torch.int32, device="cuda")
+    f = tf.indexer_logits(pplan, PP.view(), prs, prp, piq, pww, plog, n_valid=pnv, prepare=True)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    reps = 20
+    pe = [TimingEvent() for _ in range(reps + 1)]
+    pe[0].record()
+    for i in range(reps):
+        f()
+        pe[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([pe[i].elapsed_time(pe[i + 1]) for i in range(reps)])) * 1e3
+    flops = sum(2 * pw.H * pw.Dk * (t // 4 + 1) for _, t in pw.rows)
+    tfl = flops / (us * 1e-6) / 1e12
+    prefill = {"call": "tf_indexer_logits", "launches": list(ENTRIES["indexer_prefill"][0]),
+               "workload": pw.name, "rows": len(pw.rows), "keys": pld, "us": round(us, 2), "reps": reps,
+               "causal_flop": flops,
+               "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "traffic": load_traffic("indexer_prefill")}}
+    step = bench_prefill_step(tf, pw, pplan, PP, prs, prp, piq, pww, plog, pnv, args.prefill_reps)
+    del PP, plog
+    torch.cuda.empty_cache()
+    cpu = cpu_baseline_prefill(pw, args.cpu_seconds, step["us_per_step"]) if with_cpu else None
+    return prefill, step, cpu
 
 
 def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
@@ -413,7 +456,7 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
     for r, (_, t) in enumerate(pw.rows):                               # exact: tokens s <= t of the selected blocks
         b = blk[r][blk[r] >= 0].astype(np.int64)
         sel += int(np.minimum(4, np.maximum(0, t + 1 - 4 * b)).sum())
-    attn_flop = sel * 4 * pw.Hq * 576
+    attn_flop = sel * 2 * pw.Hq * (576 + 512)                         # S over 576 dims, P.V over 512
     idx_flop = int(sum(2 * pw.H * pw.Dk * int(n) for n in nvh))
     def mfma(flop, t_us):
         a = flop / (t_us * 1e-6) / 1e12
@@ -574,7 +617,7 @@ def bench_dense(tf, reps):
     torch.cuda.synchronize()
     us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
     tokens = sum(min(t + 1, 4 * nb) for _, t in dw.rows)
-    flop = tokens * 4 * dw.Hq * 576
+    flop = tokens * 2 * dw.Hq * (576 + 512)
     a = flop / (us * 1e-6) / 1e12
     del P
     return {"call": "tf_dense_mla_attn", "launches": list(ENTRIES["attention_dense"][0]),
@@ -584,6 +627,233 @@ def bench_dense(tf, reps):
             "gathered_GBps": round(tokens * ROW_BYTES / (us * 1e-6) / 1e9, 1),
             "roofline": {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic("attention_dense")}}
+
+
+C4_TRAFFIC_FILE = "traffic_shared_prefix_decode_8x1M_12caches.json"
+
+
+def bench_shared_prefix(tf, reps=5):
+    """Decode over 12 caches of 8 streams that share a 1,048,576-token prefix by page
+    reference (2,048 shared pages + one private tail page each). One token's step runs the
+    decode path once per cache (write -> indexer -> top-k -> attention), the caches one
+    after another as a model's layers would; an event between every call. Per cache the
+    attention gathers 8 x 2,048 selected rows (18.9 MB) and the indexer scans each row's
+    262,144 + tail keys, of which the shared 2,048 pages' keys (67.1 MB) are the same
+    bytes for all 8 rows."""
+    import numpy as np
+    import torch
+
+    from synth import TAG_LATENT, TAG_PKEY
+    from synth.configs import LAT, ROPE, ROW, shared_prefix_decode
+    from synth.device import _rid, alloc_pool, fill_bf16, populate, query_inputs
+    wl = shared_prefix_decode(0)
+    plan = tf.kv_pool_plan(tf.geom(wl.n_caches, wl.Dk))
+    log(f"setup: {wl.name}: pool {wl.n_pages} pages x {plan.page_bytes} B")
+    P = alloc_pool(wl, plan)
+    populate(P)
+    rows = wl.rows
+    R = len(rows)
+    ld = max(t // 4 + 1 for _, t in rows)
+    scale = 1.0 / math.sqrt(576.0)
+    logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(R, dtype=torch.int32, device="cuda")
+    blocks = torch.empty((R, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, wl.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, wl.Hq), dtype=torch.float32, device="cuda")
+    kidx = torch.tensor([t // 4 for _, t in rows], dtype=torch.int32, device="cuda")
+    per_cache = []
+    keep = []
+    for c in range(wl.n_caches):
+        rs, rp, iq, w, q = query_inputs(wl, c, rows)
+        lat = torch.empty((R, LAT), dtype=torch.bfloat16, device="cuda")
+        rope = torch.empty((R, ROPE), dtype=torch.bfloat16, device="cuda")
+        key = torch.empty((R, wl.Dk), dtype=torch.bfloat16, device="cuda")
+        for i, (b, t) in enumerate(rows):
+            r0 = _rid(c, b, t)                      # tail rows are the stream's own (owner b)
+            fill_bf16(lat[i:], 1, LAT, wl.seed, TAG_LATENT, r0 * ROW, ROW, ROW)
+            fill_bf16(rope[i:], 1, ROPE, wl.seed, TAG_LATENT, r0 * ROW + LAT, ROW, ROW)
+            fill_bf16(key[i:], 1, wl.Dk, wl.seed, TAG_PKEY, _rid(c, b, t // 4) * wl.Dk, wl.Dk, wl.Dk)
+        v = P.view(c)
+        keep.append((rs, rp, iq, w, q, lat, rope, key))
+        per_cache.append([
+            tf.latent_write(plan, v, rs, rp, lat, rope, pkey_stream=rs, pkey_idx=kidx, pkeys=key, prepare=True),
+            tf.indexer_logits(plan, v, rs, rp, iq, w, logits, n_valid=nv, prepare=True),
+            tf.topk_blocks(logits, nv, wl.k, blocks, prepare=True),
+            tf.sparse_mla_attn(plan, v, rs, rp, q, scale, blocks, out, lse, prepare=True),
+        ])
+    for _ in range(2):
+        for calls in per_cache:
+            for f in calls:
+                f()
+    torch.cuda.synchronize()
+    C = wl.n_caches
+    ev = [[[TimingEvent() for _ in range(5)] for _ in range(C)] for _ in range(reps)]
+    for i in range(reps):
+        for c in range(C):
+            ev[i][c][0].record()
+            for j, f in enumerate(per_cache[c]):
+                f()
+                ev[i][c][j + 1].record()
+    torch.cuda.synchronize()
+    names = ["write", "indexer", "topk", "attention"]
+    us = {n: [[ev[i][c][j].elapsed_time(ev[i][c][j + 1]) * 1e3 for c in range(C)] for i in range(reps)]
+          for j, n in enumerate(names)}
+    token_us = _mean([ev[i][0][0].elapsed_time(ev[i][C - 1][4]) * 1e3 for i in range(reps)])
+    att = [_mean([us["attention"][i][c] for i in range(reps)]) for c in range(C)]
+    idx = [_mean([us["indexer"][i][c] for i in range(reps)]) for c in range(C)]
+    lat_bytes = R * wl.k * 4 * ROW_BYTES
+    scanned = sum(t // 4 + 1 for _, t in rows) * wl.Dk * 2
+    unique = (wl.shared_tokens // 4 + sum(t // 4 + 1 - wl.shared_tokens // 4 for _, t in rows)) * wl.Dk * 2
+    att_gbs = [lat_bytes / (u * 1e-6) / 1e9 for u in att]
+    res = {"workload": wl.name, "caches": C, "streams": R, "shared_tokens": wl.shared_tokens,
+           "tails": [t + 1 - wl.shared_tokens for _, t in rows], "reps": reps,
+           "token_step_us": round(token_us, 1),
+           "calls_us_mean_over_caches": {n: round(_mean([x for r in us[n] for x in r]), 2) for n in names},
+           "attention": {"call": "tf_sparse_mla_attn", "latent_bytes_per_cache": lat_bytes,
+                         "us_per_cache": [round(u, 2) for u in att],
+                         "latent_GBps_per_cache": [round(g, 1) for g in att_gbs],
+                         "latent_GBps_mean": round(_mean(att_gbs), 1),
+                         "frac_hbm_mean": round(_mean(att_gbs) / HBM_PEAK_GBS, 4)},
+           "indexer": {"call": "tf_indexer_logits", "us_per_cache": [round(u, 2) for u in idx],
+                       "keys_scanned_bytes_per_cache": scanned, "unique_key_bytes_per_cache": unique,
+                       "scanned_GBps_mean": round(scanned / (_mean(idx) * 1e-6) / 1e9, 1),
+                       "unique_GBps_mean": round(unique / (_mean(idx) * 1e-6) / 1e9, 1),
+                       "traffic": load_traffic("indexer", C4_TRAFFIC_FILE)}}
+    del per_cache, keep, P
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_adaptive_prefill(tf):
+    """The 390,000-token prompt in fp8 rows, prefilled in 464 adaptive chunks
+    (chunk(L) = clamp(round_down_256(2e8 / L), 256, 2048), the rule tf_prefill_chunk
+    applies): per chunk, write its rows and keys, score its rows against every visible
+    key, top-512, attention with 32 heads. All inputs are generated into HBM first; an
+    event between every call. Then the snapshot of the first 262,144 rows (every plane
+    and the keys [0, 65,536)) into another stream's pages, timed alone."""
+    import numpy as np
+    import torch
+
+    from synth import TAG_LAT8, TAG_LATENT, TAG_PKEY, TAG_SCALE8
+    from synth.configs import LAT, ROPE, ROW, adaptive_prefill
+    from synth.device import _rid, alloc_pool, fill_bf16, fill_e4m3, fill_scale8, query_inputs
+    wl = adaptive_prefill(0)
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk, fp8=True))
+    N = wl.lengths[0]
+    log(f"setup: {wl.name}: pool {wl.n_pages} pages x {plan.page_bytes} B; generating {N} rows of inputs")
+    P = alloc_pool(wl, plan)
+    view = P.view()
+    sched, L = [], 0
+    while L < N:
+        T = tf.prefill_chunk(L, N - L)
+        sched.append((L, T))
+        L += T
+    r0 = _rid(0, 0, 0)
+    lat = torch.empty((N, LAT), dtype=torch.uint8, device="cuda")
+    fill_e4m3(lat, N, LAT, wl.seed, TAG_LAT8, r0 * LAT, LAT)
+    sc = torch.empty(N, dtype=torch.float32, device="cuda")
+    fill_scale8(sc, N, wl.seed, TAG_SCALE8, r0)
+    rope = torch.empty((N, ROPE), dtype=torch.bfloat16, device="cuda")
+    fill_bf16(rope, N, ROPE, wl.seed, TAG_LATENT, r0 * ROW + LAT, ROW, ROW)
+    nk = (N + 3) // 4
+    keys = torch.empty((nk, wl.Dk), dtype=torch.bfloat16, device="cuda")
+    fill_bf16(keys, nk, wl.Dk, wl.seed, TAG_PKEY, r0 * wl.Dk, wl.Dk, wl.Dk)
+    kstream = torch.zeros(nk, dtype=torch.int32, device="cuda")
+    kidx = torch.arange(nk, dtype=torch.int32, device="cuda")
+    rs, rp, iq, w, q = query_inputs(wl, 0, [(0, t) for t in range(N)])
+    max_log = max(T * ((L + T - 1) // 4 + 1) for L, T in sched)
+    logbuf = torch.empty(max_log, dtype=torch.float32, device="cuda")
+    nv = torch.empty(2048, dtype=torch.int32, device="cuda")
+    blocks = torch.empty((2048, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((2048, wl.Hq, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2048, wl.Hq), dtype=torch.float32, device="cuda")
+    tws = torch.empty(max(16, max(tf.topk_workspace_bytes(T, (L + T - 1) // 4 + 1, wl.k) for L, T in sched)),
+                      dtype=torch.uint8, device="cuda")
+    aws = torch.empty(max(16, max(tf.attn_workspace_bytes(T, wl.Hq, wl.k) for _, T in sched)), dtype=torch.uint8,
+                      device="cuda")
+    scale = 1.0 / math.sqrt(576.0)
+    torch.cuda.synchronize()
+
+    def chunk_calls(L, T):
+        ld = (L + T - 1) // 4 + 1
+        j0, j1 = (L + 3) // 4, (L + T + 3) // 4
+        lg = logbuf[:T * ld].view(T, ld)
+        return [
+            lambda: tf.latent_write(plan, view, rs[L:L + T], rp[L:L + T], lat[L:L + T], rope[L:L + T],
+                                    row_scale=sc[L:L + T], pkey_stream=kstream[j0:j1], pkey_idx=kidx[j0:j1],
+                                    pkeys=keys[j0:j1]),
+            lambda: tf.indexer_logits(plan, view, rs[L:L + T], rp[L:L + T], iq[L:L + T], w[L:L + T], lg,
+                                      n_valid=nv[:T]),
+            lambda: tf.topk_blocks(lg, nv[:T], wl.k, blocks[:T], ws=tws),
+            lambda: tf.sparse_mla_attn(plan, view, rs[L:L + T], rp[L:L + T], q[L:L + T], scale, blocks[:T],
+                                       out[:T], lse[:T], ws=aws),
+        ]
+    log(f"adaptive prefill: {len(sched)} chunks")
+    ev = [[TimingEvent() for _ in range(5)] for _ in sched]
+    for i, (L, T) in enumerate(sched):
+        ev[i][0].record()
+        for j, f in enumerate(chunk_calls(L, T)):
+            f()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    names = ["write", "indexer", "topk", "attention"]
+    call_us = [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for j in range(4)] for i in range(len(sched))]
+    chunk_us = [sum(c) for c in call_us]
+    total_us = ev[0][0].elapsed_time(ev[-1][4]) * 1e3
+    bands = {}
+    idx_flop = att_flop = 0
+    for (L, T), cu, c4 in zip(sched, chunk_us, call_us):
+        b = bands.setdefault(T, {"chunks": 0, "tokens": 0, "us": 0.0, "first_L": L, "indexer_us": 0.0,
+                                 "attention_us": 0.0})
+        b["chunks"] += 1
+        b["tokens"] += T
+        b["us"] += cu
+        b["indexer_us"] += c4[1]
+        b["attention_us"] += c4[3]
+        # causal work of the chunk: every row t scores t // 4 + 1 keys; attention reads
+        # min(2,048, t + 1) tokens (512 blocks, the row's own last block cut at t)
+        idx_flop += 2 * wl.H * wl.Dk * sum(t // 4 + 1 for t in range(L, L + T))
+        att_flop += 2 * wl.Hq * (576 + 512) * sum(min(4 * wl.k, t + 1) for t in range(L, L + T))
+    for T, b in bands.items():
+        b["us"] = round(b["us"], 1)
+        b["indexer_us"] = round(b["indexer_us"], 1)
+        b["attention_us"] = round(b["attention_us"], 1)
+        b["tok_per_s"] = round(b["tokens"] / (b["us"] * 1e-6), 1)
+    calls_total = {n: round(sum(c[j] for c in call_us), 1) for j, n in enumerate(names)}
+    # snapshot of the first 262,144 rows of stream 0 into stream 1's pages
+    at = 262144
+    src = torch.tensor([0], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([1], dtype=torch.int32, device="cuda")
+    f = tf.snapshot_copy(plan, view, view, src, dst, at, prepare=True)
+    f()
+    torch.cuda.synchronize()
+    sreps = 10
+    se = [TimingEvent() for _ in range(sreps + 1)]
+    se[0].record()
+    for i in range(sreps):
+        f()
+        se[i + 1].record()
+    torch.cuda.synchronize()
+    snap_us = _mean([se[i].elapsed_time(se[i + 1]) * 1e3 for i in range(sreps)])
+    snap_bytes = at * (plan.lat_row_bytes + 4 + plan.rope_row_bytes) + (at // 4) * plan.pkey_row_bytes
+    res = {"workload": wl.name, "tokens": N, "chunks": len(sched), "total_us": round(total_us, 1),
+           "tok_per_s": round(N / (total_us * 1e-6), 1), "calls_total_us": calls_total,
+           "bands_by_chunk_size": {str(T): bands[T] for T in sorted(bands, reverse=True)},
+           "indexer": {"causal_flop": idx_flop, "us": calls_total["indexer"],
+                       "TFLOPs": round(idx_flop / (calls_total["indexer"] * 1e-6) / 1e12, 1),
+                       "frac_mfma": round(idx_flop / (calls_total["indexer"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                          4)},
+           "attention": {"flop": att_flop, "us": calls_total["attention"],
+                         "TFLOPs": round(att_flop / (calls_total["attention"] * 1e-6) / 1e12, 1),
+                         "frac_mfma": round(att_flop / (calls_total["attention"] * 1e-6) / 1e12
+                                            / MFMA_BF16_PEAK_TFLOPS, 4)},
+           "snapshot": {"call": "tf_snapshot_copy", "at": at, "bytes_each_way": snap_bytes, "us": round(snap_us, 2),
+                        "reps": sreps, "GBps_read_plus_written": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+           "timing": "an event between every call; inputs generated into HBM before the first chunk"}
+    del P, lat, sc, rope, keys, q, iq, w, logbuf, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
@@ -596,11 +866,7 @@ def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
     from oracle import workload as ow
     from oracle.attention import selected_tokens
     from synth import bf16_to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = _host_threads()
     log("cpu baseline: generating inputs")
     q_i = bf16_to_f64(wl.iq_bits(0, rows))
     w_i = wl.weights(0, rows).astype(np.float64)
@@ -628,20 +894,78 @@ def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
         busy += time.perf_counter() - t0
         steps += 1
     sec = busy / steps
-    return {"value": round(step_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(step_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads["cores"], "kind": "oracle",
             "sample": f"{steps} whole decode steps of the same workload ({len(rows)} rows: logits over {ld} "
                       f"keys each, exact top-{wl.k}, attention over the selected rows), {busy:.1f} s",
-            "seconds_per_step": round(sec, 4), "cpu_model": _cpu_model()}
+            "seconds_per_step": round(sec, 4), "blas_threads": threads["blas_threads"], "cpu_model": _cpu_model()}
+
+
+def _host_threads():
+    """Host cores this process may run on (its affinity mask), and the threads the BLAS
+    behind numpy uses (the oracle's only multi-threaded part)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return {"cores": cores, "blas_threads": blas}
 
 
 def _cpu_model():
+    """The host CPU's model name, with its family / model / stepping numbers (a model name
+    alone can be as short as the vendor's brand)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
     except Exception:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(ids)})" if name else None
+
+
+def cpu_baseline_prefill(pw, seconds, gpu_step_us):
+    """The oracle (fp64 numpy) on rows of the prefill chunk: logits over every visible key,
+    exact top-k, attention over the selected rows, one sampled row at a time for about
+    `seconds`; the chunk's time is extrapolated from the per-row rate (labelled so)."""
+    import numpy as np
+    from oracle import indexer_logits, sparse_mla, topk_blocks
+    from oracle import workload as ow
+    from synth import bf16_to_f64
+    threads = _host_threads()
+    log("cpu baseline (prefill chunk): generating inputs")
+    rng = np.random.default_rng(5)
+    order = rng.permutation(len(pw.rows))
+    ld = pw.rows[-1][1] // 4 + 1
+    keys = ow.keys_of(pw, 0, 0, ld)
+    reader = ow.rows_reader(pw, 0, 0)
+    scale = 1.0 / math.sqrt(576.0)
+    n, busy = 0, 0.0
+    while busy < seconds and n < len(order):
+        r = int(order[n])
+        row = [pw.rows[r]]
+        q_i = bf16_to_f64(pw.iq_bits(0, row))
+        w_i = pw.weights(0, row).astype(np.float64)
+        q_a = bf16_to_f64(pw.q_bits(0, row))
+        t = row[0][1]
+        t0 = time.perf_counter()
+        lg = indexer_logits(q_i, w_i, [keys], [t], ld)
+        blk = topk_blocks(lg, [min(t // 4 + 1, ld)], pw.k)
+        sparse_mla(q_a, lambda _r, S: reader(S), blk, [t], scale)
+        busy += time.perf_counter() - t0
+        n += 1
+    per_row = busy / n
+    T = len(pw.rows)
+    return {"value": round(1.0 / per_row, 3), "unit": "rows/s", "cores": threads["cores"], "kind": "oracle",
+            "sample": f"{n} randomly chosen rows of the {T}-row chunk (logits over up to {ld} keys, exact "
+                      f"top-{pw.k}, attention over the selected rows), {busy:.1f} s",
+            "chunk_seconds_extrapolated": round(per_row * T, 2), "extrapolated": True,
+            "gpu_chunk_us": gpu_step_us, "gpu_over_cpu": round(per_row * T / (gpu_step_us * 1e-6), 1),
+            "blas_threads": threads["blas_threads"], "cpu_model": _cpu_model()}
 
 
 # ---------------------------------------------------------------------- profile summaries
@@ -728,7 +1052,7 @@ def _pmc(db, counter):
     return {n: next((v for v in gs.values() if len(v) == timed), max(gs.values(), key=len)) for n, gs in by.items()}
 
 
-def summarize_pmc(fetch_db, write_db, command):
+def summarize_pmc(fetch_db, write_db, command, traffic_file=TRAFFIC_FILE):
     """HBM bytes per launch of each entry point from one FETCH_SIZE and one WRITE_SIZE
     pass (KiB per dispatch), each scaled by what the same counter reads for the
     calibration stream (CAL_BYTES read and CAL_BYTES written by one torch.neg)."""
@@ -756,7 +1080,7 @@ def summarize_pmc(fetch_db, write_db, command):
                                                "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)},
            "entries": entries}
     os.makedirs(PROFILES, exist_ok=True)
-    path = os.path.join(PROFILES, TRAFFIC_FILE)
+    path = os.path.join(PROFILES, traffic_file)
     json.dump(res, open(path, "w"), indent=1)
     print(json.dumps(res, indent=1))
 
