@@ -71,6 +71,9 @@ SIGNATURES = {
     "tf_topk_in_candidates": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp,
                                        ctypes.c_size_t, _vp]),
     "tf_topk_in_candidates_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32]),
+    "tf_sparse_mla_attn_noalloc": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
+                                            ctypes.c_float, _vp, _c_i32, _vp, _vp, _vp]),
+    "tf_sparse_mla_attn_noalloc_max_bytes": (ctypes.c_size_t, []),
     "tf_dense_mla_attn": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _c_i32,
                                    ctypes.c_float, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_attn_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
@@ -286,6 +289,19 @@ def sparse_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, bloc
                                        n_heads, float(softmax_scale), _ptr(blocks), k, _ptr(out), _ptr(lse),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
                 prepare, keep=(ws,))
+
+
+def sparse_mla_attn_noalloc(plan, kv, row_stream, row_pos, q, softmax_scale: float, blocks, out, lse=None,
+                            stream=None, prepare=False):
+    """tf_sparse_mla_attn with the library's fixed scratch in place of a workspace: nothing is allocated."""
+    n_rows, n_heads = q.shape[0], q.shape[1]
+    return _run("tf_sparse_mla_attn_noalloc", (ctypes.byref(plan), kv, n_rows, _ptr(row_stream), _ptr(row_pos),
+                                               _ptr(q), n_heads, float(softmax_scale), _ptr(blocks), blocks.shape[1],
+                                               _ptr(out), _ptr(lse), _stream(stream)), prepare)
+
+
+def sparse_mla_attn_noalloc_max_bytes() -> int:
+    return int(lib().tf_sparse_mla_attn_noalloc_max_bytes())
 
 
 def dense_mla_attn(plan, kv, row_stream, row_pos, q, softmax_scale: float, n_blocks: int, out, lse=None, ws=None,

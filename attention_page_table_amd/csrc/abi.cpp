@@ -387,6 +387,29 @@ extern "C" tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t
                      k, out, lse, ws, ws_bytes, (hipStream_t)stream);
 }
 
+extern "C" size_t tf_sparse_mla_attn_noalloc_max_bytes(void) { return attn_scratch_bytes(); }
+
+extern "C" tf_status tf_sparse_mla_attn_noalloc(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
+                                                const int32_t* row_stream, const int32_t* row_pos,
+                                                const void* q, int32_t n_heads, float softmax_scale,
+                                                const int32_t* blocks, int32_t k, float* out, float* lse,
+                                                void* stream) {
+  clear_error();
+  tf_status s = check_sparse_attn("tf_sparse_mla_attn_noalloc", p, kv, n_rows, row_stream, row_pos, q, n_heads,
+                                  softmax_scale, blocks, k, out);
+  if (s != TF_OK || n_rows == 0) return s;
+  const size_t need = attn_ws_bytes(n_rows, n_heads, k);
+  if (need > attn_scratch_bytes())
+    return set_error(TF_E_RANGE,
+                     "tf_sparse_mla_attn_noalloc: %d rows x %d heads x k=%d need %zu bytes of split partials, the "
+                     "library's fixed scratch holds %zu; split the rows over calls or use tf_sparse_mla_attn",
+                     n_rows, n_heads, k, need, attn_scratch_bytes());
+  void* ws = nullptr;
+  if (need > 0 && (s = attn_scratch(&ws)) != TF_OK) return s;
+  return launch_attn(p, make_view(p, kv), n_rows, row_stream, row_pos, q, n_heads, softmax_scale, blocks,
+                     k, out, lse, ws, need, (hipStream_t)stream);
+}
+
 extern "C" tf_status tf_dense_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
                                        const int32_t* row_stream, const int32_t* row_pos,
                                        const void* q, int32_t n_heads, float softmax_scale,

@@ -39,6 +39,8 @@
 // block list; the others test for the list at run time.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace tf {
@@ -1091,6 +1093,36 @@ static SplitPlan pick_split(int32_t n_rows, int32_t n_heads, int32_t k, bool fp8
   p.n_units = n_rows * p.nsplit;
   p.grid = p.ngroups == 1 ? p.n_units : ((p.n_units + 7) / 8) * 16;
   return p;
+}
+
+// Split partials of the allocation-free entry point: a file-scope device array, one
+// copy per GPU, held until the process ends. Host code never passes the array's name to
+// a kernel (on the host it names a stand-in, not device memory): the device address is
+// looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = 32u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+size_t attn_scratch_bytes() { return kScratchBytes; }
+
+tf_status attn_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(TF_E_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(TF_E_DEVICE, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(TF_E_DEVICE, "hipGetSymbolAddress of the attention scratch failed on device %d: %s", dev,
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TF_OK;
 }
 
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k) {

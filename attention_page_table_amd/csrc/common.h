@@ -83,6 +83,10 @@ tf_status launch_topk_merge(int32_t B, int32_t nb, int64_t ncap, int32_t n_rows,
 tf_status launch_group_max(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid, int32_t g,
                            float* scores, int64_t ldg, int32_t* n_groups, hipStream_t st);
 size_t attn_ws_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
+// the fixed device scratch of the allocation-free sparse pass (attention.hip): its size,
+// and its address on the current device (looked up once per device)
+size_t attn_scratch_bytes();
+tf_status attn_scratch(void** ptr);
 // blocks == nullptr runs the dense pass over the first k pooled blocks
 tf_status launch_attn(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
                       const int32_t* row_pos, const void* q, int32_t n_heads, float scale,

@@ -284,6 +284,24 @@ tf_status tf_sparse_mla_attn(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
                              const int32_t* blocks, int32_t k, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* The sparse pass for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results as tf_sparse_mla_attn, bit for bit, with no workspace
+ * argument. Its split partials live in a fixed scratch array inside the library
+ * (tf_sparse_mla_attn_noalloc_max_bytes() bytes, 32 MiB, one copy per GPU, held
+ * until the process ends); a call whose partials need more (see
+ * tf_attn_workspace_bytes) is refused with TF_E_RANGE before any launch. The call
+ * allocates nothing. Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (two streams, or two threads) race and must be serialized by
+ * the caller. Nothing in the scratch needs clearing between calls; a call writes
+ * every partial it reads. Other arguments and errors as for tf_sparse_mla_attn. */
+tf_status tf_sparse_mla_attn_noalloc(const tf_plan* p, tf_kv_view kv, int32_t n_rows,
+                                     const int32_t* row_stream, const int32_t* row_pos,
+                                     const void* q, int32_t n_heads, float softmax_scale,
+                                     const int32_t* blocks, int32_t k, float* out, float* lse,
+                                     void* stream);
+size_t tf_sparse_mla_attn_noalloc_max_bytes(void);
+
 /* Dense absorbed-MLA attention [#1142, "What stays as it is", and the kernel
  * list of its proposal: the page-table kernels read the latent for dense
  * chunks as well as for the sparse gather]: the short-context pass that skips

@@ -214,3 +214,21 @@ def test_page_table_check_refuses_ids_outside_the_pool():
     with pytest.raises(tf.TFError):
         tf.view(None, None, 4, 6, pt_host=pt)
 
+
+def test_noalloc_sparse_pass_refuses_beyond_its_scratch():
+    """The allocation-free sparse pass refuses, before any launch, a call whose split
+    partials exceed its fixed scratch (no pointer is dereferenced)."""
+    L = tf.lib()
+    p = tf.kv_pool_plan(tf.geom(1, 64))
+    fake = ctypes.c_void_p(0x1000)
+    v = tf.tf_kv_view(fake, None, 4, 4, 16, 0)
+    cap = tf.sparse_mla_attn_noalloc_max_bytes()
+    assert cap == 32 << 20
+    assert tf.attn_workspace_bytes(4096, 16, 2048) > cap
+    assert L.tf_sparse_mla_attn_noalloc(ctypes.byref(p), v, 4096, fake, fake, fake, 16, 1.0, fake, 2048, fake, None,
+                                        None) == tf.TF_E_RANGE
+    assert "fixed scratch" in L.tf_last_error().decode()
+    assert L.tf_sparse_mla_attn_noalloc(ctypes.byref(p), v, 8, fake, fake, fake, 33, 1.0, fake, 64, fake, None,
+                                        None) == tf.TF_E_UNSUPPORTED
+    assert L.tf_sparse_mla_attn_noalloc(ctypes.byref(p), v, 0, None, None, None, 32, 1.0, None, 64, None, None,
+                                        None) == tf.TF_OK
