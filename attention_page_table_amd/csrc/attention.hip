@@ -1003,7 +1003,9 @@ constexpr int kMergeBatch = 16;
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
   __shared__ float wgt[64];
   __shared__ float tot[2];
-  const int r = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
+  // row r's merges run on the XCD that wrote its partials: workgroup h * n_rows + r (a
+  // row's splits are n_rows workgroups apart, and workgroup i runs on XCD i mod 8)
+  const int r = blockIdx.x % a.n_rows, h = blockIdx.x / a.n_rows;
   const int c4 = 4 * threadIdx.x;
   const float* po = a.part_o + ((int64_t)r * a.nsplit * 32 + h) * kLatent + c4;
   float4 v[kMergeBatch];

@@ -769,7 +769,7 @@ def bench_adaptive_prefill(tf):
     lse = torch.empty((2048, wl.Hq), dtype=torch.float32, device="cuda")
     tws = torch.empty(max(16, max(tf.topk_workspace_bytes(T, (L + T - 1) // 4 + 1, wl.k) for L, T in sched)),
                       dtype=torch.uint8, device="cuda")
-    aws = torch.empty(max(16, max(tf.attn_workspace_bytes(T, wl.Hq, wl.k) for _, T in sched)), dtype=torch.uint8,
+    aws = torch.zeros(max(16, max(tf.attn_workspace_bytes(T, wl.Hq, wl.k) for _, T in sched)), dtype=torch.uint8,
                       device="cuda")
     scale = 1.0 / math.sqrt(576.0)
     torch.cuda.synchronize()
