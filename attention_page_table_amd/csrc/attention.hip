@@ -546,6 +546,7 @@ static_assert(2 * sizeof(AttnSharedW) <= 160 * 1024, "two sliced 32-head workgro
 
 constexpr float kLazy = 8.f;
 
+template <bool FP8>
 __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t* tt, int it, float scale_log2,
                                                   int tid) {
   constexpr int TPH = 8, TPT = kTileTok / TPH;
@@ -576,9 +577,10 @@ __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t
   for (int e = 0; e < TPT; ++e) {
     const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
     lsum += pe;
-    const __bf16 hi = bf16_rne(pe);
+    const float pv = FP8 ? pe * sh.tsc[p * TPT + e] : pe;   // fp8 rows: the row scale joins P
+    const __bf16 hi = bf16_rne(pv);
     phv[e] = hi;
-    plv[e] = bf16_rne(pe - bf16_to_f(hi));
+    plv[e] = bf16_rne(pv - bf16_to_f(hi));
   }
   *(bv_t*)&sh.p_hi[h][p * TPT] = phv;
   *(bv_t*)&sh.p_lo[h][p * TPT] = plv;
@@ -595,7 +597,12 @@ __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t
   }
 }
 
-template <bool DENSE>
+// FP8: rows of e4m3 codes and a row scale. A lane gathers its token's 64 codes at dims
+// 128 w + 64 g .. + 63 (four 16-byte loads, where bf16 rows take eight) and widens them
+// to bf16 exactly in registers (two codes per instruction); its k-steps take those dims
+// in order (the queries are read to match), the row scale multiplies the latent part of
+// S and joins P in the softmax.
+template <bool DENSE, bool FP8>
 __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh) {
   typedef Frag<32> F;
   const int tid = threadIdx.x;
@@ -649,8 +656,10 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
     const int head = h0 + F::a_row(lane);
     const __bf16* qr = a.q + ((int64_t)r * a.n_heads + head) * kRow;
 #pragma unroll
-    for (int i = 0; i < F::kSteps; ++i)
-      aq[i] = head < a.n_heads ? *(const bf16x8*)(qr + F::ks_dim(wave, i, F::a_half(lane))) : bf16x8{};
+    for (int i = 0; i < F::kSteps; ++i) {
+      const int d = FP8 && i < 8 ? 128 * wave + 64 * F::a_half(lane) + 8 * i : F::ks_dim(wave, i, F::a_half(lane));
+      aq[i] = head < a.n_heads ? *(const bf16x8*)(qr + d) : bf16x8{};
+    }
   }
   F::acc_t o[F::kNT];
 #pragma unroll
@@ -661,37 +670,73 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
   // n = the token, k = the wave's dims (8 latent steps, then its rope step)
   const int tok = F::tok_of_lane(wave, lane), g = F::a_half(lane);
   bf16x8 kvr[F::kSteps];
+  uint4 raw[4];   // fp8: the token's 64 codes of this lane's dims, widened when S needs them
+  float sc = 0.f;  // fp8: the token's row scale
   // a token that is not attended (or whose page the table does not name) gets zeros:
   // its probability is 0, and 0 x V must not meet unwritten bytes
   auto gather = [&](int tile) __attribute__((always_inline)) {
     const int32_t e = sh.tt[tile * kTileTok + tok];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < F::kSteps; ++i) kvr[i] = bf16x8{};
+      for (int j = 0; j < 4; ++j) raw[j] = make_uint4(0, 0, 0, 0);
+      kvr[8] = bf16x8{};
+      sc = 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < F::kSteps; ++i) kvr[i] = bf16x8{};
+    }
     if (e >= 0) {
       const int64_t base = row_base(a, e);
       const char* rowp = a.v.pool + base + (int64_t)(e & 511) * a.lat_row_bytes;
       const char* ropep = a.v.pool + base + a.off_rope + (int64_t)(e & 511) * (kRope * 2);
+      if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kvr[i] = *(const bf16x8*)(rowp + (wave * 128 + 16 * i + 8 * g) * 2);
+        for (int j = 0; j < 4; ++j) raw[j] = *(const uint4*)(rowp + wave * 128 + 64 * g + 16 * j);
+        sc = *(const float*)(a.v.pool + base + a.off_scale + 4LL * (e & 511));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kvr[i] = *(const bf16x8*)(rowp + (wave * 128 + 16 * i + 8 * g) * 2);
+      }
       kvr[8] = *(const bf16x8*)(ropep + (16 * wave + 8 * g) * 2);
+    }
+  };
+  // fp8: codes 8i .. 8i + 7 of the lane's 64 as bf16 (exact: every e4m3 value is a bf16).
+  // Each conversion turns the two codes of one half of a dword into one dword of two
+  // bf16, the lower address in the lower half; the fragment is assembled from those
+  // dwords as they are.
+  auto widen = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w0 = (i & 1) ? raw[i >> 1].z : raw[i >> 1].x;
+      const uint32_t w1 = (i & 1) ? raw[i >> 1].w : raw[i >> 1].y;
+      u32x4 d;
+      d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false));
+      d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true));
+      d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false));
+      d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true));
+      kvr[i] = __builtin_bit_cast(bf16x8, d);
     }
   };
   if (ntiles > 0) gather(0);
   __bf16* vt = &sh.vt[wave][0][0];
   for (int it = 0; it < ntiles; ++it) {
     // ---- S partial from the registers ------------------------------------------------
+    if constexpr (FP8) widen();
+    const float sc_tile = sc;
     F::acc_t accl{}, accr{};
 #pragma unroll
     for (int i = 0; i < 8; ++i) accl = F::mfma(aq[i], kvr[i], accl);
     accr = F::mfma(aq[8], kvr[8], accr);
     // ---- the slice's latent columns to this wave's LDS region, then the next gather ----
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(bf16x8*)&vt[tok * kVS + 16 * i + 8 * g] = kvr[i];
+    for (int i = 0; i < 8; ++i) *(bf16x8*)&vt[tok * kVS + (FP8 ? 64 * g + 8 * i : 16 * i + 8 * g)] = kvr[i];
     if (it + 1 < ntiles) gather(it + 1);
 #pragma unroll
-    for (int i = 0; i < F::kAccN; ++i) sh.spart[wave][F::row_of(i, lane)][tok] = accl[i] + accr[i];
+    for (int i = 0; i < F::kAccN; ++i)
+      sh.spart[wave][F::row_of(i, lane)][tok] = FP8 ? accl[i] * sc_tile + accr[i] : accl[i] + accr[i];
+    if (FP8 && wave == 0 && lane < kTileTok) sh.tsc[tok] = sc_tile;   // the tile's row scales, for P
     __syncthreads();
-    softmax_tile_lazy(sh, sh.tt + it * kTileTok, it, a.scale_log2, tid);
+    softmax_tile_lazy<FP8>(sh, sh.tt + it * kTileTok, it, a.scale_log2, tid);
     __syncthreads();
     {
       if (__builtin_amdgcn_readfirstlane(sh.moved[it & 1]) != 0) {   // some head's max moved
@@ -727,13 +772,23 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
 
 __global__ __launch_bounds__(256, 2) void attn_kernel_w32(AttnArgs a) {
   __shared__ AttnSharedW sh;
-  attn_w32_body<false>(a, sh);
+  attn_w32_body<false, false>(a, sh);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_kernel_w32_fp8(AttnArgs a) {
+  __shared__ AttnSharedW sh;
+  attn_w32_body<false, true>(a, sh);
 }
 
 // The dense pass's instance: no block list to read (slot j is block j).
 __global__ __launch_bounds__(256, 2) void attn_dense_kernel_w32(AttnArgs a) {
   __shared__ AttnSharedW sh;
-  attn_w32_body<true>(a, sh);
+  attn_w32_body<true, false>(a, sh);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_dense_kernel_w32_fp8(AttnArgs a) {
+  __shared__ AttnSharedW sh;
+  attn_w32_body<true, true>(a, sh);
 }
 
 // ---- decode: every row of the workgroup in LDS at once ------------------------------------
@@ -1170,7 +1225,8 @@ tf_status launch_attn(const tf_plan* pl, const DevView& v, int32_t n_rows, const
     if (fp8) hipLaunchKernelGGL((attn_kernel<16, true>), dim3(p.grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_kernel<16, false>), dim3(p.grid), dim3(256), 0, st, a);
   } else {
-    if (fp8) hipLaunchKernelGGL((attn_kernel<32, true>), dim3(p.grid), dim3(256), 0, st, a);
+    if (fp8 && blocks) hipLaunchKernelGGL(attn_kernel_w32_fp8, dim3(p.grid), dim3(256), 0, st, a);
+    else if (fp8) hipLaunchKernelGGL(attn_dense_kernel_w32_fp8, dim3(p.grid), dim3(256), 0, st, a);
     else if (blocks) hipLaunchKernelGGL(attn_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(attn_dense_kernel_w32, dim3(p.grid), dim3(256), 0, st, a);
   }

@@ -331,11 +331,13 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 #pragma unroll
     for (int r = 0; r < RH; ++r) {
       const float s = weighted_relu_sum<H>(&wv[t][r * H], acc, r * H);
+      // non-temporal: the logits stream out past L2, which keeps the key chunks other
+      // workgroups of the XCD read
       if (M == kOpen) {
-        optr[t][r][kt] = s;
+        __builtin_nontemporal_store(s, &optr[t][r][kt]);
       } else {
         const float v = key < rnc[t][r] ? (pg_ok ? s : qnan) : ninf;
-        if (M == kFull || key < ke) optr[t][r][kt] = v;
+        if (M == kFull || key < ke) __builtin_nontemporal_store(v, &optr[t][r][kt]);
       }
     }
   };

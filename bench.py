@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     ap.add_argument("--traffic-file", default=TRAFFIC_FILE, help="profiles/ file --summarize-pmc writes")
+    ap.add_argument("--summarize-counters", metavar="DB", help="per-kernel averages of a rocprofv3 --pmc pass")
+    ap.add_argument("--kernels", default="", help="comma list of kernel-name prefixes for --summarize-counters")
     ap.add_argument("--label", default="decode_step")
     ap.add_argument("--command", default="")
     ap.add_argument("--bench-json", help="the line an unprofiled run of the same command printed")
@@ -163,6 +165,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.command, args.traffic_file)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.label, args.command, args.kernels.split(","))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -1035,6 +1040,50 @@ def summarize_trace(db, label, command, bench_json=None):
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"{label}.txt")
     open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
+
+
+def summarize_counters(db, label, command, prefixes):
+    """Per-dispatch values of every counter a rocprofv3 --pmc pass collected, for the
+    kernels whose names start with one of `prefixes` (grouped by kernel and grid size;
+    averaged over dispatches), written to profiles/<label>.txt with the command that
+    produced them. A counter comes as one value per hardware instance (shader engine,
+    XCD); a dispatch's value is the sum over instances, except GRBM_GUI_ACTIVE, whose
+    maximum is the dispatch's active cycles. Where the pass holds
+    SQ_VALU_MFMA_BUSY_CYCLES, MFMA utilisation is reported as rocprofv3's MfmaUtil
+    defines it: MFMA-busy cycles over all SIMDs / (active cycles x SIMDs)."""
+    c = sqlite3.connect(db)
+    per = {}
+    for name, g, did, cn, v in c.execute("select p.name, k.grid_x * k.grid_y * k.grid_z, p.dispatch_id, p.counter_name, "
+                                         "p.counter_value from pmc_events p join kernels k "
+                                         "on p.dispatch_id = k.dispatch_id"):
+        n = _short(name)
+        if not any(n.startswith(x) or n.startswith("void " + x) for x in prefixes if x):
+            continue
+        d = per.setdefault((n, g), {}).setdefault(did, {})
+        if cn == "GRBM_GUI_ACTIVE":
+            d[cn] = max(d.get(cn, 0.0), float(v))
+        else:
+            d[cn] = d.get(cn, 0.0) + float(v)
+    lines = [f"# rocprofv3 counters: {label}", f"# command: {command}", "",
+             "# per dispatch: counters summed over hardware instances (GRBM_GUI_ACTIVE: their maximum), "
+             "averaged over dispatches"]
+    for (n, g), ds in sorted(per.items()):
+        names = sorted({cn for d in ds.values() for cn in d})
+        lines.append(f"{n} [grid {g}]  ({len(ds)} dispatches)")
+        avg = {cn: sum(d.get(cn, 0.0) for d in ds.values()) / len(ds) for cn in names}
+        for cn in names:
+            lines.append(f"  {cn:36s} {avg[cn]:20.1f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            util = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] * SIMDS)
+            lines.append(f"  {'MFMA utilisation (MfmaUtil)':36s} {util:19.1f}%")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            lines.append(f"  {'bf16 MFMA flop (MOPS x 512)':36s} {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:20.4g}")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, f"{label}.txt"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
