@@ -65,8 +65,10 @@ ENTRIES = {
     "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4>"), "topk.hip"),
     "topk_prefill": (("tf::topk_row_kernel<28>",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
-    "attention_prefill": (("tf::attn_kernel",), "attention.hip"),
+    "attention_prefill": (("tf::attn_kernel_w32",), "attention.hip"),
     "attention_dense": (("tf::attn_dense_kernel_w32",), "attention.hip"),
+    "attention_fp8": (("tf::attn_kernel_w32_fp8",), "attention.hip"),
+    "snapshot": (("tf::snapshot_kernel",), "write.hip"),
 }
 TRAFFIC_FILE = "traffic_bench_decode_8x131072_prefill_indexer_2048_at_100000.json"
 CAL_KERNEL = "neg_kernel"      # torch.neg over CAL_BYTES of float32: a plain streaming copy
@@ -974,9 +976,16 @@ def cpu_baseline_prefill(pw, seconds, gpu_step_us):
 
 
 # ---------------------------------------------------------------------- profile summaries
+def _matches(name, p):
+    """A kernel's short name belongs to a listed kernel name p: the same name, or p with
+    template arguments (or a grid tag) appended."""
+    n = name[5:] if name.startswith("void ") else name
+    return n == p or n.startswith(p + " [") or (n.startswith(p + "<") if "<" not in p else n.startswith(p))
+
+
 def _entry_of(name):
     for e, (prefixes, _) in ENTRIES.items():
-        if any(name.startswith(p) or name.startswith("void " + p) for p in prefixes):
+        if any(_matches(name, p) for p in prefixes):
             return e
     return None
 
@@ -1107,9 +1116,15 @@ def summarize_pmc(fetch_db, write_db, command, traffic_file=TRAFFIC_FILE):
     calibration stream (CAL_BYTES read and CAL_BYTES written by one torch.neg)."""
     fetch, write = _pmc(fetch_db, "FETCH_SIZE"), _pmc(write_db, "WRITE_SIZE")
     cal = [k for k in fetch if CAL_KERNEL in k]
-    assert cal, "the calibration kernel is missing from the FETCH_SIZE pass"
-    cf = CAL_BYTES / (fetch[cal[0]][0] * 1024.0)
-    cw = CAL_BYTES / (write[[k for k in write if CAL_KERNEL in k][0]][0] * 1024.0)
+    if cal:
+        cf = CAL_BYTES / (fetch[cal[0]][0] * 1024.0)
+        cw = CAL_BYTES / (write[[k for k in write if CAL_KERNEL in k][0]][0] * 1024.0)
+        calib = {"kernel": cal[0], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES}
+    else:   # a pass over a leg without the stream: the scales of the decode pass's file
+        assert traffic_file != TRAFFIC_FILE, "the calibration kernel is missing from the FETCH_SIZE pass"
+        prev = json.load(open(os.path.join(PROFILES, TRAFFIC_FILE)))["calibration"]
+        cf, cw = prev["fetch_scale"], prev["write_scale"]
+        calib = {"from": TRAFFIC_FILE, "kernel": prev["kernel"], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES}
     entries = {}
     for n in fetch:
         e = _entry_of(n)
@@ -1125,8 +1140,7 @@ def summarize_pmc(fetch_db, write_db, command, traffic_file=TRAFFIC_FILE):
         d["fetch_bytes_per_launch"] = round(fb)
         d["write_bytes_per_launch"] = round(wb)
         d["hbm_bytes_per_launch"] = round(fb + wb)
-    res = {"command": command, "calibration": {"kernel": cal[0], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES,
-                                               "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)},
+    res = {"command": command, "calibration": dict(calib, fetch_scale=round(cf, 4), write_scale=round(cw, 4)),
            "entries": entries}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, traffic_file)
