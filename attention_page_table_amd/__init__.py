@@ -66,6 +66,9 @@ SIGNATURES = {
     "tf_indexer_topk": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32, _c_i64,
                                  _c_i32, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_indexer_topk_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
+    "tf_indexer_topk_fused": (_c_i32, [ctypes.POINTER(tf_plan), tf_kv_view, _c_i32, _vp, _vp, _vp, _vp, _c_i32,
+                                       _c_i64, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tf_indexer_topk_fused_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
     "tf_candidate_groups": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]),
     "tf_candidate_groups_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i64, _c_i32, _c_i32]),
     "tf_topk_in_candidates": (_c_i32, [_vp, _c_i64, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp,
@@ -249,6 +252,22 @@ def indexer_topk(plan, keys, row_stream, row_pos, q, w, ld: int, k: int, key_blo
     return _run("tf_indexer_topk", (ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
                                     _ptr(w), H, int(ld), int(k), int(key_block), _ptr(blocks), _ptr(n_valid),
                                     _ptr(ws), ws.numel(), _stream(stream)), prepare, keep=(ws,))
+
+
+def indexer_topk_fused_workspace_bytes(n_rows: int, ld: int, k: int, n_heads: int) -> int:
+    return int(lib().tf_indexer_topk_fused_workspace_bytes(n_rows, ld, k, n_heads))
+
+
+def indexer_topk_fused(plan, keys, row_stream, row_pos, q, w, ld: int, k: int, blocks, n_valid=None, ws=None,
+                       stream=None, prepare=False):
+    n_rows, H = w.shape
+    if ws is None:
+        import torch
+        ws = torch.empty(max(256, indexer_topk_fused_workspace_bytes(n_rows, ld, k, H)), dtype=torch.uint8,
+                         device=w.device)
+    return _run("tf_indexer_topk_fused", (ctypes.byref(plan), keys, n_rows, _ptr(row_stream), _ptr(row_pos), _ptr(q),
+                                          _ptr(w), H, int(ld), int(k), _ptr(blocks), _ptr(n_valid), _ptr(ws),
+                                          ws.numel(), _stream(stream)), prepare, keep=(ws,))
 
 
 def candidate_groups(logits, n_valid, group: int, n_cand: int, cand, ws=None, stream=None, prepare=False):

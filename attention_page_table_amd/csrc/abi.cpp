@@ -272,6 +272,41 @@ extern "C" tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t 
   return launch_topk_merge(key_block, (int32_t)nb, ld, n_rows, nv, k, blocks, cand, st);
 }
 
+extern "C" size_t tf_indexer_topk_fused_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t n_heads) {
+  if (n_rows <= 0 || ld <= 0 || k <= 0 || (n_heads != 4 && n_heads != 8 && n_heads != 16)) return 0;
+  return indexer_topk_fused_ws_bytes(n_heads, n_rows, ld, k);
+}
+
+extern "C" tf_status tf_indexer_topk_fused(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
+                                           const int32_t* row_stream, const int32_t* row_pos, const void* q,
+                                           const float* w, int32_t n_heads, int64_t ld, int32_t k, int32_t* blocks,
+                                           int32_t* n_valid, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  tf_status s;
+  if ((s = check_plan(p)) != TF_OK) return s;
+  if ((s = check_view(p, keys, "keys")) != TF_OK) return s;
+  if (n_rows < 0) return set_error(TF_E_INVAL, "tf_indexer_topk_fused: n_rows < 0");
+  if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_indexer_topk_fused: n_rows=%d, at most 65535 a call", n_rows);
+  if (ld < 1 || ld > (1LL << 24)) return set_error(TF_E_RANGE, "tf_indexer_topk_fused: ld=%lld", (long long)ld);
+  if (k < 1 || k > 2048) return set_error(TF_E_RANGE, "tf_indexer_topk_fused: k=%d, need 1..2048", k);
+  if (n_heads != 4 && n_heads != 8 && n_heads != 16)
+    return set_error(TF_E_UNSUPPORTED, "tf_indexer_topk_fused: n_heads=%d, built for 4, 8 or 16", n_heads);
+  if (n_rows == 0) return TF_OK;
+  if (!row_stream || !row_pos || !q || !w || !blocks)
+    return set_error(TF_E_INVAL, "tf_indexer_topk_fused: row_stream, row_pos, q, w and blocks are required");
+  if (!aligned16(q)) return set_error(TF_E_INVAL, "tf_indexer_topk_fused: q must be 16-byte aligned");
+  const size_t need = indexer_topk_fused_ws_bytes(n_heads, n_rows, ld, k);
+  if (need == (size_t)-1)
+    return set_error(TF_E_RANGE, "tf_indexer_topk_fused: no top-k block size fits %d rows of %lld keys, k=%d", n_rows,
+                     (long long)ld, k);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255) != 0)
+    return set_error(TF_E_INVAL,
+                     "tf_indexer_topk_fused: a 256-byte aligned workspace of %zu bytes is needed, got %zu", need,
+                     ws_bytes);
+  return launch_indexer_topk_fused(p, make_view(p, keys), n_rows, row_stream, row_pos, q, w, n_heads, ld, k, blocks,
+                                   n_valid, ws, (hipStream_t)stream);
+}
+
 // Candidate groups' workspace: the group scores (rows padded to whole quads), the
 // rows' group counts, then the top-k's own.
 static int64_t group_stride(int64_t ld, int32_t g) { return ((ld + g - 1) / g + 3) / 4 * 4; }

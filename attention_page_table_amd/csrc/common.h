@@ -68,6 +68,12 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows,
                          const float* w, int32_t n_heads, float* logits, int64_t ld,
                          int32_t* n_valid, hipStream_t st, int64_t key0, int64_t kend, int64_t ncap,
                          bool window);
+// fused indexer + top-k (indexer.hip): sampled threshold, filtered scoring, selection
+size_t indexer_topk_fused_ws_bytes(int32_t n_heads, int32_t n_rows, int64_t ld, int32_t k);
+tf_status launch_indexer_topk_fused(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+                                    const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
+                                    int64_t ld, int32_t k, int32_t* blocks, int32_t* n_valid, void* ws,
+                                    hipStream_t st);
 size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k);
 // cand (nullable): keys outside the row's candidate groups of `group` keys read as -inf
 tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int32_t* n_valid,

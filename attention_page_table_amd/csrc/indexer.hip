@@ -23,7 +23,7 @@
 //    the row's page ids preloaded across the lanes.
 #include <type_traits>
 
-#include "common.h"
+#include "select.h"
 
 namespace tf {
 
@@ -45,7 +45,20 @@ struct IdxArgs {
   int32_t* n_valid;
   int32_t keys_per_wg;   // multiple of 128
   int32_t n_kgroups;
+  int32_t page_step;     // sampled scoring: logical page i is page i * page_step of the stream
+  // filtered scoring: a key whose logit's order key is at least thr[row] goes to its
+  // (row, key group) region of cap slots, in key order; cand_cnt counts them all
+  const uint32_t* thr;
+  uint32_t* cand_key;    // [n_rows][n_kgroups][cap] order keys
+  int32_t* cand_idx;     // [n_rows][n_kgroups][cap] key indices
+  int32_t* cand_cnt;     // [n_rows][n_kgroups]
+  int32_t cap;
 };
+
+// What a tile-kernel instance computes (one instance each, so that profiles keep the
+// launches apart): every key, one key block of a key-blocked call, a page sample, or
+// the filtered candidates.
+constexpr int kWhole = 0, kWindow = 1, kSample = 2, kFilter = 3;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -66,23 +79,49 @@ __device__ __forceinline__ float weighted_relu_sum(const float* w, const A& acc,
   return s[0] + s[1];
 }
 
+// The row's visible keys: n_c = min(t / 4 + 1, ncap). Sampled scoring counts the
+// logical keys of the sampled pages below n_c (a prefix of the logical keys, since
+// page i of the sample is page i * page_step).
+template <bool SAMPLED = false>
 __device__ __forceinline__ int nc_of(const IdxArgs& a, int row) {
   const int pos = a.row_pos[row];
   if (pos < 0) return 0;
-  const int64_t nc = (int64_t)pos / kPoolRatio + 1;
-  return (int)(nc < a.ncap ? nc : a.ncap);
+  int64_t nc = (int64_t)pos / kPoolRatio + 1;
+  if (nc > a.ncap) nc = a.ncap;
+  if (!SAMPLED) return (int)nc;
+  const int64_t pl = (nc - 1) / kKeysPerPage;   // page of the last visible key
+  const int64_t il = pl / a.page_step;           // last sampled page at or below it
+  const int64_t c = il * kKeysPerPage + (il * a.page_step == pl ? nc - pl * kKeysPerPage : kKeysPerPage);
+  return (int)(c < a.kend ? c : a.kend);
+}
+
+// Appends this lane's key to its row's region when `pass`, in lane order within each
+// half-wave (half g holds the keys of one row): slot = count so far + passing lanes
+// below it in the half. cnt is uniform over the half and grows by the half's passes.
+__device__ __forceinline__ void append_candidate(const IdxArgs& a, bool pass, uint32_t u, int64_t key, int g,
+                                                 int32_t off, int32_t& cnt) {
+  const uint64_t m = __ballot(pass);
+  const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+  const uint32_t below = g ? __builtin_amdgcn_mbcnt_hi(hi, 0u) : __builtin_amdgcn_mbcnt_lo(lo, 0u);
+  const int32_t slot = cnt + (int32_t)below;
+  if (pass && slot < a.cap) {
+    a.cand_key[off + slot] = u;
+    a.cand_idx[off + slot] = (int32_t)key;
+  }
+  cnt += (int32_t)__builtin_popcount(g ? hi : lo);
 }
 
 // ---- per-row path: one wave streams one row over keys [kb, ke) ---------------------------
 // A-rows with bit 2 clear carry the row's heads (head 4 * (m / 8) + m % 4), the others are
 // zero; lanes 0..31 then hold every head of key n = lane in accumulators 0..H-1.
-template <int H, int D>
-__device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke, int lane, bool spec_page = false,
-                              int spec_page_all = -1) {
+template <int H, int D, int KIND>
+__device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke, int lane, int kg,
+                              bool spec_page = false, int spec_page_all = -1) {
+  constexpr bool FILTER = KIND == kFilter, SAMPLED = KIND == kSample;
   constexpr int KS = D / 16;
   const int g = lane >> 5, n = lane & 31;
   const int b = a.row_stream[row];
-  const int nc = nc_of(a, row);
+  const int nc = nc_of<SAMPLED>(a, row);
   const float ninf = -__builtin_inff();
   float* out = a.logits + (int64_t)row * a.ldo;
   bf16x8 aq[KS];
@@ -107,7 +146,7 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
     const int pb = b >= 0 && b < a.v.n_streams ? __builtin_amdgcn_readlane(spec_page_all, b) : -1;
     my_page = lane == 0 ? pb : -1;
   } else {
-    my_page = page_of(a.v, b, p0 + lane);
+    my_page = page_of(a.v, b, SAMPLED ? (p0 + lane) * a.page_step : p0 + lane);
   }
   auto page_at = [&](int64_t kt) { return __builtin_amdgcn_readlane(my_page, (int)(kt / kKeysPerPage) - p0); };
   auto load = [&](int64_t kt, bf16x8 (&bf)[KS]) {
@@ -121,6 +160,10 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
       for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
     }
   };
+  // filtered: the row's threshold, region and count (lanes 0..31 hold the keys)
+  const uint32_t thr = FILTER ? a.thr[row] : 0u;
+  const int32_t off = FILTER ? (row * a.n_kgroups + kg) * a.cap : 0;
+  int32_t cnt = 0;
   // three subtiles in flight: slot s holds subtile kb + 32 (3i + s)
   auto step = [&](int64_t kt, bf16x8 (&cur)[KS]) {
     f32x16 acc = {};
@@ -130,7 +173,12 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
     if (kt + 96 < kend) load(kt + 96, cur);   // refill the slot three subtiles ahead
     const float s = weighted_relu_sum<H>(wv, acc, 0);
     const int64_t key = kt + n;
-    if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
+    if constexpr (FILTER) {
+      const uint32_t u = order_key(pg >= 0 ? s : __builtin_nanf(""));
+      append_candidate(a, g == 0 && key < ke && key < nc && u >= thr, u, key, g, off, cnt);
+    } else {
+      if (g == 0 && key < ke) out[key] = key < nc ? (pg >= 0 ? s : __builtin_nanf("")) : ninf;
+    }
   };
   bf16x8 s0[KS], s1[KS], s2[KS];
   if (kb < kend) load(kb, s0);
@@ -141,14 +189,19 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
     if (kt + 32 < kend) step(kt + 32, s1);
     if (kt + 64 < kend) step(kt + 64, s2);
   }
+  if constexpr (FILTER) {
+    if (lane == 0) a.cand_cnt[row * a.n_kgroups + kg] = cnt;
+    return;
+  }
   // keys past the compressed length
   for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) out[key] = ninf;
 }
 
 // Per-row kernel: wave w of workgroup (key group kg, row group rg) takes row 4 rg + w.
 // The row groups of one key group run on one XCD (workgroups 8 apart).
-template <int H, int D>
+template <int H, int D, int KIND>
 __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
+  constexpr bool SAMPLED = KIND == kSample;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_rg = (a.n_rows + 3) / 4;
   const int id = blockIdx.x;
@@ -164,14 +217,14 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
   const bool spec = a.keys_per_wg == kKeysPerPage && a.v.n_streams <= 64;
   int spec_all = -1;
   if (spec) {
-    const int pi = (int)(kb / kKeysPerPage);
+    const int pi = (int)(kb / kKeysPerPage) * (SAMPLED ? a.page_step : 1);
     if (lane < a.v.n_streams && pi < a.v.pt_stride) {
       const int pg = a.v.pt ? a.v.pt[(int64_t)lane * a.v.pt_stride + pi] : lane * a.v.pt_stride + pi;
       spec_all = pg >= 0 && pg < a.v.n_pages ? pg : -1;
     }
   }
-  if (kg == 0 && a.n_valid && lane == 0) a.n_valid[row] = nc_of(a, row);
-  index_one_row<H, D>(a, row, kb, ke, lane, spec, spec_all);
+  if (kg == 0 && a.n_valid && lane == 0) a.n_valid[row] = nc_of<SAMPLED>(a, row);
+  index_one_row<H, D, KIND>(a, row, kb, ke, lane, kg, spec, spec_all);
 }
 
 // ---- tile path -----------------------------------------------------------------------------
@@ -188,10 +241,12 @@ __device__ __forceinline__ int swz(int j, int c) {
   return j * CH + (c ^ (j & (CH - 1)));
 }
 
-// WINDOW names the instance that scores one key block of a key-blocked call, so that
-// profiles keep its launches apart from whole-range ones; the code is the same.
-template <int H, int D, int MT, bool WINDOW>
+// KIND: kWhole, kWindow and kSample store logits (the same code; the sample's pages are
+// strided through page_step); kFilter appends the keys at or above each row's threshold
+// to the row's region for this workgroup's key group instead.
+template <int H, int D, int MT, int KIND>
 __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
+  constexpr bool FILTER = KIND == kFilter, SAMPLED = KIND == kSample;
   constexpr int RPT = 32 / H;   // query rows per MFMA tile
   constexpr int RH = 16 / H;    // rows per half-wave in the accumulators
   constexpr int KS = D / 16;    // MFMA k-steps
@@ -211,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   const int wave_row0 = row_base + wave * (MT * RPT);
 
   if (blockIdx.x == 0 && a.n_valid && tid < ROWS && row_base + tid < a.n_rows)
-    a.n_valid[row_base + tid] = nc_of(a, row_base + tid);
+    a.n_valid[row_base + tid] = nc_of<SAMPLED>(a, row_base + tid);
 
   // all rows of the workgroup valid and of one stream?
   if (tid == 0) uniform_flag = 1;
@@ -224,9 +279,9 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
     for (int rr = wave; rr < ROWS; rr += 4) {
       const int row = row_base + rr;
       if (row < a.n_rows) {
-        if (H == 16) index_one_row<16, D>(a, row, kb, ke, lane);
-        else if (H == 8) index_one_row<8, D>(a, row, kb, ke, lane);
-        else index_one_row<4, D>(a, row, kb, ke, lane);
+        if (H == 16) index_one_row<16, D, KIND>(a, row, kb, ke, lane, blockIdx.x);
+        else if (H == 8) index_one_row<8, D, KIND>(a, row, kb, ke, lane, blockIdx.x);
+        else index_one_row<4, D, KIND>(a, row, kb, ke, lane, blockIdx.x);
       }
     }
     return;
@@ -238,9 +293,9 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < RH; ++r) rnc[t][r] = nc_of(a, wave_row0 + t * RPT + g * RH + r);
+    for (int r = 0; r < RH; ++r) rnc[t][r] = nc_of<SAMPLED>(a, wave_row0 + t * RPT + g * RH + r);
   for (int rr = 0; rr < ROWS; ++rr) {
-    const int c = nc_of(a, row_base + rr);
+    const int c = nc_of<SAMPLED>(a, row_base + rr);
     nc_max = c > nc_max ? c : nc_max;
     nc_min = c < nc_min ? c : nc_min;
   }
@@ -248,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
 
   // page ids of the key range
   const int p0 = (int)(kb / kKeysPerPage);
-  if (tid < kMaxPages) pg_lds[tid] = page_of(a.v, b0, p0 + tid);
+  if (tid < kMaxPages) pg_lds[tid] = page_of(a.v, b0, SAMPLED ? (p0 + tid) * a.page_step : p0 + tid);
 
   // A fragments: lane supplies A-row m = n; m = 8a + 4b + c maps to tile row
   // b*RH + (4a+c)/H and head (4a+c)%H.
@@ -274,10 +329,22 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
     for (int i = 0; i < 16; ++i) wv[t][i] = a.w[(int64_t)(wave_row0 + t * RPT + g * RH + i / H) * H + (i % H)];
   // this lane's output rows, at key n
   float* optr[MT][RH];
+  // filtered: each row's threshold, region offset and count so far
+  uint32_t thr[MT][RH];
+  int32_t coff[MT][RH], cnt[MT][RH];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < RH; ++r) optr[t][r] = a.logits + (int64_t)(wave_row0 + t * RPT + g * RH + r) * a.ldo + n;
+    for (int r = 0; r < RH; ++r) {
+      const int row = wave_row0 + t * RPT + g * RH + r;
+      if constexpr (FILTER) {
+        thr[t][r] = a.thr[row];
+        coff[t][r] = (row * a.n_kgroups + (int)blockIdx.x) * a.cap;
+        cnt[t][r] = 0;
+      } else {
+        optr[t][r] = a.logits + (int64_t)row * a.ldo + n;
+      }
+    }
   __syncthreads();
 
   // global -> LDS loads of one 128-key chunk (one page, since kb is a multiple of
@@ -325,12 +392,19 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   constexpr int kOpen = 0, kFull = 1, kPart = 2;
   constexpr int kSubs = kChunk / 32;
   constexpr bool kPipe = H == 16 || D == 64;
+  constexpr int kValu = FILTER ? 6 : 4;   // head-sum (and append) instructions per MFMA
   auto epilogue = [&](const f32x16& acc, int t, int64_t kt, bool pg_ok, auto mode) __attribute__((always_inline)) {
     constexpr int M = decltype(mode)::value;
     const int64_t key = kt + n;
 #pragma unroll
     for (int r = 0; r < RH; ++r) {
       const float s = weighted_relu_sum<H>(&wv[t][r * H], acc, r * H);
+      if constexpr (FILTER) {
+        const bool in = M == kOpen || (key < rnc[t][r] && (M == kFull || key < ke));
+        const uint32_t u = order_key(M == kOpen || pg_ok ? s : qnan);
+        append_candidate(a, in && u >= thr[t][r], u, key, g, coff[t][r], cnt[t][r]);
+        continue;
+      }
       // non-temporal: the logits stream out past L2, which keeps the key chunks other
       // workgroups of the XCD read
       if (M == kOpen) {
@@ -362,12 +436,12 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
           if (t > 0) epilogue(acc[t - 1], t - 1, kt, pg_ok, mode);
           else if (sub > 0) epilogue(acc[MT - 1], MT - 1, kt - 32, pg_ok, mode);
           // pin the interleave: per MFMA, the B read that refills its register (last
-          // tile only) and four instructions of the previous tile's head sum
+          // tile only) and kValu instructions of the previous tile's head sum
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (t == MT - 1 && sub + 1 < kSubs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (t > 0 || sub > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            if (t > 0 || sub > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
           }
         } else {
           epilogue(acc[t], t, kt, pg_ok, mode);
@@ -380,6 +454,15 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
   // next chunk's loads (its stores), so that the next barrier waits for the loads only
   auto chunk = [&](int64_t kt, const __bf16* src) __attribute__((always_inline)) -> bool {
     const bool pg_ok = pg_lds[(int)(kt / kKeysPerPage) - p0] >= 0;
+    if constexpr (FILTER) {   // a data-dependent number of stores: the next wait takes them all
+      if (kt + kChunk <= ke && pg_ok && kt + kChunk <= nc_min)
+        chunk_body(kt, src, pg_ok, std::integral_constant<int, kOpen>{});
+      else if (kt + kChunk <= ke)
+        chunk_body(kt, src, pg_ok, std::integral_constant<int, kFull>{});
+      else
+        chunk_body(kt, src, pg_ok, std::integral_constant<int, kPart>{});
+      return false;
+    }
     if (kt + kChunk <= ke && pg_ok && kt + kChunk <= nc_min) {
       chunk_body(kt, src, pg_ok, std::integral_constant<int, kOpen>{});
       return true;
@@ -420,58 +503,88 @@ __global__ __launch_bounds__(256, 2) void indexer_tile_kernel(IdxArgs a) {
     fixed = chunk(kt + kChunk, kc1.k) && kt + 2 * kChunk < kend;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (FILTER) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < RH; ++r)
+        if (n == 0) a.cand_cnt[(wave_row0 + t * RPT + g * RH + r) * a.n_kgroups + (int)blockIdx.x] = cnt[t][r];
+    return;
+  }
   // keys past every row's compressed length
   const int64_t kf = kend > kb ? kend : kb;
   for (int rr = wave; rr < ROWS; rr += 4)
     for (int64_t key = kf + lane; key < ke; key += 64) a.logits[(int64_t)(row_base + rr) * a.ldo + key] = ninf;
 }
 
-template <int H, int D>
-static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st, bool window) {
-  constexpr int RPT = 32 / H;
-  if (n_rows >= 64) {
-    constexpr int MT = 2;
-    constexpr int ROWS = 4 * MT * RPT;
-    const int64_t rgroups = (n_rows + ROWS - 1) / ROWS;
-    // about 1,024 workgroups (four per CU), each over a multiple of 128 keys (at most 4,096)
-    const int64_t nk = a.kend - a.key0;
-    int64_t kpw = (nk * rgroups + 1023) / 1024;
+// Launch shape of a scoring call over nk keys: the tile kernel (n_rows >= 64) with
+// about 1,024 workgroups (four per CU), each over a multiple of 128 keys (at most
+// 4,096), or the row kernel with about 2,048 waves (eight per CU keep more key loads in
+// flight than four), a wave's range spanning at most 64 pages.
+struct IdxShape {
+  bool tile;
+  int64_t kpw, kgroups, grid_x, grid_y;
+};
+
+// wg_target: workgroups the tile kernel aims at; min_kpw: a floor on the keys per
+// workgroup or wave (a multiple of 128).
+static IdxShape idx_shape(int H, int32_t n_rows, int64_t nk, int64_t wg_target = 1024, int64_t min_kpw = 128) {
+  IdxShape s;
+  s.tile = n_rows >= 64;
+  int64_t kpw;
+  if (s.tile) {
+    const int rows = 4 * 2 * (32 / H);   // 4 waves x MT = 2 tiles x 32 / H rows
+    const int64_t rgroups = (n_rows + rows - 1) / rows;
+    kpw = (nk * rgroups + wg_target - 1) / wg_target;
     kpw = (kpw + 127) / 128 * 128;
-    if (kpw < 128) kpw = 128;
-    if (kpw > 4096) kpw = 4096;
-    a.keys_per_wg = (int32_t)kpw;
-    const int64_t kgroups = (nk + kpw - 1) / kpw;
-    a.n_kgroups = (int32_t)kgroups;
-    if (rgroups > 65535) return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows for one launch");
-    if (window)
-      hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, true>), dim3((unsigned)kgroups, (unsigned)rgroups),
-                         dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, false>), dim3((unsigned)kgroups, (unsigned)rgroups),
-                         dim3(256), 0, st, a);
+    kpw = kpw < min_kpw ? min_kpw : kpw;
+    kpw = kpw < 128 ? 128 : (kpw > 4096 ? 4096 : kpw);
+    s.kgroups = (nk + kpw - 1) / kpw;
+    s.grid_x = s.kgroups;
+    s.grid_y = rgroups;
   } else {
-    // each wave one row; about 2,048 waves in all (eight per CU keep more key loads in
-    // flight than four); a wave's range spans at most 64 pages
-    const int n_rg = (n_rows + 3) / 4;
-    const int64_t nk = a.kend - a.key0;
-    int64_t kpw = (nk * n_rows + 2047) / 2048;
+    kpw = (nk * n_rows + 2047) / 2048;
     kpw = (kpw + 127) / 128 * 128;
-    if (kpw < 128) kpw = 128;
-    if (kpw > 64 * 128) kpw = 64 * 128;
-    a.keys_per_wg = (int32_t)kpw;
-    const int64_t kgroups = (nk + kpw - 1) / kpw;
-    a.n_kgroups = (int32_t)kgroups;
-    const int64_t grid = ((kgroups + 7) / 8) * 8 * n_rg;
-    if (grid > 0x7fffffffLL) return set_error(TF_E_RANGE, "tf_indexer_logits: too many keys for one launch");
-    hipLaunchKernelGGL((indexer_rows_kernel<H, D>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    kpw = kpw < min_kpw ? min_kpw : kpw;
+    kpw = kpw < 128 ? 128 : (kpw > 64 * 128 ? 64 * 128 : kpw);
+    s.kgroups = (nk + kpw - 1) / kpw;
+    s.grid_x = ((s.kgroups + 7) / 8) * 8 * ((n_rows + 3) / 4);
+    s.grid_y = 1;
+  }
+  s.kpw = kpw;
+  return s;
+}
+
+template <int H, int D>
+static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st, int kind, int64_t wg_target = 1024,
+                           int64_t min_kpw = 128) {
+  const IdxShape sh = idx_shape(H, n_rows, a.kend - a.key0, wg_target, min_kpw);
+  a.keys_per_wg = (int32_t)sh.kpw;
+  a.n_kgroups = (int32_t)sh.kgroups;
+  if (sh.tile) {
+    constexpr int MT = 2;
+    if (sh.grid_y > 65535) return set_error(TF_E_RANGE, "tf_indexer_logits: too many rows for one launch");
+    const dim3 grid((unsigned)sh.grid_x, (unsigned)sh.grid_y);
+    switch (kind) {
+      case kWhole: hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, kWhole>), grid, dim3(256), 0, st, a); break;
+      case kWindow: hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, kWindow>), grid, dim3(256), 0, st, a); break;
+      case kSample: hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, kSample>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((indexer_tile_kernel<H, D, MT, kFilter>), grid, dim3(256), 0, st, a); break;
+    }
+  } else {
+    if (sh.grid_x > 0x7fffffffLL) return set_error(TF_E_RANGE, "tf_indexer_logits: too many keys for one launch");
+    const dim3 grid((unsigned)sh.grid_x);
+    switch (kind) {
+      case kSample: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kSample>), grid, dim3(256), 0, st, a); break;
+      case kFilter: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kFilter>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kWhole>), grid, dim3(256), 0, st, a); break;
+    }
   }
   return TF_OK;
 }
 
-tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
-                         const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
-                         float* logits, int64_t ld, int32_t* n_valid, hipStream_t st, int64_t key0,
-                         int64_t kend, int64_t ncap, bool window) {
+static IdxArgs base_args(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+                         const int32_t* row_pos, const void* q, const float* w) {
   IdxArgs a;
   a.v = v;
   a.off_pkey = p->off_pkey;
@@ -481,27 +594,568 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, con
   a.row_pos = row_pos;
   a.q = (const __bf16*)q;
   a.w = w;
+  a.logits = nullptr;
+  a.ldo = 0;
+  a.key0 = 0;
+  a.kend = 0;
+  a.ncap = 0;
+  a.n_valid = nullptr;
+  a.keys_per_wg = 128;
+  a.n_kgroups = 1;
+  a.page_step = 1;
+  a.thr = nullptr;
+  a.cand_key = nullptr;
+  a.cand_idx = nullptr;
+  a.cand_cnt = nullptr;
+  a.cap = 0;
+  return a;
+}
+
+static tf_status launch_any(const tf_plan* p, IdxArgs a, int32_t n_heads, int32_t n_rows, hipStream_t st, int kind) {
+  const int D = p->g.index_dim;
+  if (D == 128) {
+    if (n_heads == 16) return launch_hd<16, 128>(a, n_rows, st, kind);
+    if (n_heads == 8) return launch_hd<8, 128>(a, n_rows, st, kind);
+    return launch_hd<4, 128>(a, n_rows, st, kind);
+  }
+  if (n_heads == 16) return launch_hd<16, 64>(a, n_rows, st, kind);
+  if (n_heads == 8) return launch_hd<8, 64>(a, n_rows, st, kind);
+  return launch_hd<4, 64>(a, n_rows, st, kind);
+}
+
+tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+                         const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
+                         float* logits, int64_t ld, int32_t* n_valid, hipStream_t st, int64_t key0,
+                         int64_t kend, int64_t ncap, bool window) {
+  IdxArgs a = base_args(p, v, n_rows, row_stream, row_pos, q, w);
   a.logits = (float*)((uintptr_t)logits - (uintptr_t)key0 * sizeof(float));   // never read below logits
   a.ldo = ld;
   a.key0 = key0;
   a.kend = kend;
   a.ncap = ncap;
   a.n_valid = n_valid;
-  a.keys_per_wg = 128;
-  a.n_kgroups = 1;
-  const int D = p->g.index_dim;
-  tf_status s;
-  if (D == 128) {
-    if (n_heads == 16) s = launch_hd<16, 128>(a, n_rows, st, window);
-    else if (n_heads == 8) s = launch_hd<8, 128>(a, n_rows, st, window);
-    else s = launch_hd<4, 128>(a, n_rows, st, window);
-  } else {
-    if (n_heads == 16) s = launch_hd<16, 64>(a, n_rows, st, window);
-    else if (n_heads == 8) s = launch_hd<8, 64>(a, n_rows, st, window);
-    else s = launch_hd<4, 64>(a, n_rows, st, window);
-  }
+  const tf_status s = launch_any(p, a, n_heads, n_rows, st, window ? kWindow : kWhole);
   if (s != TF_OK) return s;
   return launch_status("tf_indexer_logits");
+}
+
+// ---- fused indexer + top-k [CPM, section 2.3: only per-block candidates leave the
+// scoring; topk(union) == topk(union of per-block topk)] ---------------------------------
+// Exactness needs only that at least k keys of a row reach its threshold: the k-th
+// largest logit is then at or above it, so the row's top k, ties with the k-th value
+// included, are all candidates, and their top k is the answer.
+// 1. Page sample: the tile (or row) kernel scores every step-th page of each row into a
+//    [n_rows][S] buffer (S about a sixteenth of the keys, at least 2,048), in a launch
+//    of about 512 workgroups (one round on the chip).
+// 2. Threshold: thr[r] = about the k'-th largest sampled order key (its top 16 bits),
+//    k' = min(k, the sample's share of 2k), so that about 2k of the row's keys reach it
+//    (0, which every key passes, when the sample holds at most k'). One wave a row.
+// 3. Filtered scoring: every key again, with the same arithmetic, but a key leaves the
+//    kernel only when its order key is >= thr[r], appended in key order to the region of
+//    its (row, key group): no logits reach memory.
+// 4. Selection: the top k of each row's candidates (the regions in key-group order are in
+//    key order, so the tie rule holds), one wave a row for up to 2,048 candidates, the
+//    whole workgroup for up to 32,768. A row with fewer than k candidates or an
+//    overflowed region (more passes than slots) is re-scored inside the selection kernel
+//    instead: three radix passes, a count and an emission, each scoring its keys anew.
+// Rows of at most max(4,096, 8k) keys are scored whole into the workspace and selected
+// there (the candidates would be a large share of the keys anyway).
+
+constexpr int kMaxRegions = 512;   // key groups of the filtered pass
+constexpr int kSelRows = 8;        // rows of a selection workgroup, one a wave
+constexpr int kWaveCand = 24;      // candidates a lane holds in the one-wave selection
+
+struct FusedPlan {
+  bool direct;        // short rows: score whole rows into the sample buffer and select there
+  int32_t step;       // sampled page stride
+  int64_t S;          // sampled keys per row (a multiple of 128)
+  IdxShape shape;     // the filtered pass's launch
+  int64_t min_kpw;    // its floor on keys per workgroup (at most kMaxRegions key groups)
+  int32_t cap;        // slots per (row, key group) region
+  int32_t e_thr;      // lane values of the one-wave threshold (32, 64), or 0: the block one
+  size_t off_smp, off_nvs, off_thr, off_nv, off_cnt, off_ck, off_ci, bytes;
+  size_t off_tws, tws;   // direct: the top-k's own workspace (its blocked mode on few long rows)
+};
+
+static FusedPlan fused_plan(int H, int32_t n_rows, int64_t ld, int32_t k) {
+  FusedPlan f = {};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const int64_t pages = (ld + kKeysPerPage - 1) / kKeysPerPage;
+  if (ld <= 4096 || ld <= 8 * (int64_t)k) {
+    f.direct = true;
+    f.step = 1;
+    f.S = ld;
+    f.off_smp = take((size_t)n_rows * ld * 4);
+    f.off_nv = take((size_t)n_rows * 4);
+    f.tws = topk_ws_bytes(n_rows, ld, k);
+    if (f.tws == (size_t)-1) {
+      f.bytes = (size_t)-1;
+      return f;
+    }
+    f.off_tws = take(f.tws);
+    f.bytes = at;
+    return f;
+  }
+  int64_t sp = (pages + 15) / 16;
+  if (sp < 16) sp = 16;
+  f.step = (int32_t)((pages + sp - 1) / sp);
+  sp = (pages + f.step - 1) / f.step;
+  f.S = sp * kKeysPerPage;
+  f.e_thr = f.S <= 2048 ? 32 : (f.S <= 4096 ? 64 : 0);
+  int64_t mk = (ld + kMaxRegions - 1) / kMaxRegions;
+  f.min_kpw = (mk + 127) / 128 * 128;
+  f.shape = idx_shape(H, n_rows, ld, 1024, f.min_kpw);
+  // slots: twice the passes expected of a row of ld keys (kpw * 2k / ld) plus 32, at
+  // most kpw (the sample's threshold varies a row's candidates by about a quarter)
+  int64_t cap = (int64_t)(2.0 * (double)f.shape.kpw * 2.0 * k / (double)ld) + 32;
+  cap = (cap + 3) / 4 * 4;
+  f.cap = (int32_t)(cap < f.shape.kpw ? cap : f.shape.kpw);
+  const size_t regions = (size_t)n_rows * f.shape.kgroups;
+  f.off_smp = take((size_t)n_rows * f.S * 4);
+  f.off_nvs = take((size_t)n_rows * 4);
+  f.off_thr = take((size_t)n_rows * 4);
+  f.off_nv = take((size_t)n_rows * 4);
+  f.off_cnt = take(regions * 4);
+  f.off_ck = take(regions * f.cap * 4);
+  f.off_ci = take(regions * f.cap * 4);
+  f.bytes = at;
+  return f;
+}
+
+size_t indexer_topk_fused_ws_bytes(int32_t n_heads, int32_t n_rows, int64_t ld, int32_t k) {
+  return fused_plan(n_heads, n_rows, ld, k).bytes;
+}
+
+// k' = min(k, ceil(2k n / n_c)): the sample's share of 2k candidates (n sampled keys
+// visible to a row of n_c keys)
+__device__ __forceinline__ uint32_t sample_rank(int n, int pos, int64_t ncap, int32_t k) {
+  const int64_t nc = pos < 0 ? 0 : ((int64_t)pos / kPoolRatio + 1 < ncap ? (int64_t)pos / kPoolRatio + 1 : ncap);
+  int64_t kk = nc > 0 ? (2 * (int64_t)k * n + nc - 1) / nc : k;
+  return (uint32_t)(kk < 1 ? 1 : (kk > k ? k : kk));
+}
+
+// One wave a row (four a workgroup); the sample (S <= 64 E) in registers.
+template <int E>
+__global__ __launch_bounds__(256) void fused_threshold_kernel(const float* smp, int32_t S, const int32_t* nv_s,
+                                                             const int32_t* row_pos, int64_t ncap, int32_t k,
+                                                             int32_t n_rows, uint32_t* thr) {
+  __shared__ uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.x * 4 + wid;
+  if (r >= n_rows) return;
+  int n = nv_s[r];
+  n = n < 0 ? 0 : (n > S ? S : n);
+  const uint32_t kk = sample_rank(n, row_pos[r], ncap, k);
+  if ((uint32_t)n <= kk) {   // every visible key is a candidate
+    if (lane == 0) thr[r] = 0u;
+    return;
+  }
+  // every load issued before any is used: a load inside a branch on i < n would wait
+  // for its own data before the next one starts
+  uint32_t key[E];
+  const float* row = smp + (int64_t)r * S;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = row[e * 64 + lane < n ? e * 64 + lane : n - 1];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = e * 64 + lane < n ? order_key(v[e]) : 0u;
+  uint32_t T, rem;
+  wave_select<E>(key, kk, 16, hist[wid], T, rem);
+  if (lane == 0) thr[r] = T;
+}
+
+// Long samples: one workgroup a row, the exact k'-th largest.
+template <int E>
+__global__ __launch_bounds__(kNT) void fused_threshold_block_kernel(const float* smp, int32_t S,
+                                                                   const int32_t* nv_s, const int32_t* row_pos,
+                                                                   int64_t ncap, int32_t k, uint32_t* thr) {
+  __shared__ SelShared sh;
+  const int r = blockIdx.x;
+  int n = nv_s[r];
+  n = n < 0 ? 0 : (n > S ? S : n);
+  const uint32_t kk = sample_rank(n, row_pos[r], ncap, k);
+  if ((uint32_t)n <= kk) {
+    if (threadIdx.x == 0) thr[r] = 0u;
+    return;
+  }
+  uint32_t key[E];
+  load_keys<E>(smp + (int64_t)r * S, n, true, key);
+  uint32_t T, rem;
+  radix_select<E>(key, (int)kk, sh, T, rem);
+  if (threadIdx.x == 0) thr[r] = T;
+}
+
+struct FusedSel {
+  IdxArgs a;            // the filtered pass's arguments (regions; re-scoring)
+  const int32_t* nv;    // n_c per row, from the filtered pass
+  int32_t* n_valid;     // the caller's, optional
+  int32_t k;
+  int32_t* blocks;
+};
+
+// The top k of row `row` (n_c = nv > k) by re-scoring its keys, with the filtered
+// pass's arithmetic (one row's heads on the A rows of the row kernel's layout; a
+// product's value does not depend on where its operands sit in the tile): three
+// most-significant-digit radix passes find the k-th largest order key T and how many
+// keys equal to it are taken, then a pass counts each wave's keys above and equal to T
+// and a last pass writes the selected indices, ascending. Wave w scores a contiguous
+// run of 32-key subtiles, so the waves' runs are in key order.
+template <int H, int D>
+__device__ void rescore_select(const IdxArgs& a, int row, int nv, int k, int32_t* out, SelShared& sh) {
+  constexpr int KS = D / 16;
+  const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = a.row_stream[row];
+  bf16x8 aq[KS];
+  {
+    const int u = 4 * (n >> 3) + (n & 3);
+    const bool live = ((n >> 2) & 1) == 0 && u < H;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      aq[ks] = live ? *(const bf16x8*)(a.q + ((int64_t)row * H + u) * D + ks * 16 + g * 8) : bf16x8{};
+  }
+  float wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wv[i] = i < H ? a.w[(int64_t)row * H + i] : 0.f;
+  const int n_sub = (nv + 31) / 32;
+  const int spw = (n_sub + kWaves - 1) / kWaves;
+  const int s0 = wid * spw;
+  const int s1 = s0 + spw < n_sub ? s0 + spw : n_sub;
+  auto score = [&](int sub) -> uint32_t {
+    const int64_t kt = (int64_t)sub * 32;
+    const int pg = page_of(a.v, b, (int)(kt / kKeysPerPage));
+    bf16x8 bf[KS];
+    if (pg >= 0) {
+      const char* kp = cache_block(a.v, pg) + a.off_pkey + (int64_t)((kt % kKeysPerPage) + n) * a.pkey_row_bytes + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = *(const bf16x8*)(kp + ks * 32);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bf[ks], acc, 0, 0, 0);
+    const float s = weighted_relu_sum<H>(wv, acc, 0);
+    return g == 0 && kt + n < nv ? order_key(pg >= 0 ? s : __builtin_nanf("")) : 0u;
+  };
+  uint32_t prefix = 0u, mask = 0u, rr = (uint32_t)k;
+  uint32_t* h = sh.hist[0];
+  for (int top = 32; top > 0;) {
+    const int width = top > 11 ? 11 : top, shift = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = threadIdx.x; i < kBins; i += kNT) h[i] = 0u;
+    __syncthreads();
+    for (int sub = s0; sub < s1; ++sub) {
+      const uint32_t u = score(sub);
+      if (u != 0u && (u & mask) == prefix) atomicAdd(&h[(u >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // descending bins: thread t owns bins 2047 - 2t and 2046 - 2t
+    const uint32_t c0 = h[kBins - 1 - 2 * threadIdx.x], c1 = h[kBins - 2 - 2 * threadIdx.x];
+    const uint32_t incl = wave_incl_scan(c0 + c1);
+    if (lane == 63) sh.wsum[wid] = incl;
+    __syncthreads();
+    uint32_t tot;
+    const uint32_t above = waves_before(sh.wsum, tot) + incl - (c0 + c1);
+    if (above < rr && rr <= above + c0) {
+      sh.bin = kBins - 1 - 2 * threadIdx.x;
+      sh.rem = rr - above;
+    } else if (above + c0 < rr && rr <= above + c0 + c1) {
+      sh.bin = kBins - 2 - 2 * threadIdx.x;
+      sh.rem = rr - above - c0;
+    }
+    __syncthreads();
+    prefix |= sh.bin << shift;
+    mask |= dmask << shift;
+    rr = sh.rem;
+    top = shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix, rem = rr;
+  uint32_t gt = 0u, eq = 0u;
+  for (int sub = s0; sub < s1; ++sub) {
+    const uint32_t u = score(sub);
+    gt += (uint32_t)__builtin_popcountll(__ballot(u > T));
+    eq += (uint32_t)__builtin_popcountll(__ballot(u == T));
+  }
+  uint32_t gt_b, eq_b, gt_t, eq_t;
+  block_scan2(lane == 0 ? gt : 0u, lane == 0 ? eq : 0u, sh.scan[0], gt_b, eq_b, gt_t, eq_t);
+  uint32_t gtr = __builtin_amdgcn_readlane(gt_b, 0), eqr = __builtin_amdgcn_readlane(eq_b, 0);
+  for (int sub = s0; sub < s1; ++sub) {
+    const uint32_t u = score(sub);
+    const bool is_gt = u > T, is_eq = u == T;
+    const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+    const uint32_t bg = gtr + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+    const uint32_t be = eqr + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+    const uint32_t pos = bg + (be < rem ? be : rem);
+    if ((is_gt || (is_eq && be < rem)) && pos < (uint32_t)k) out[pos] = sub * 32 + n;
+    gtr += (uint32_t)__builtin_popcountll(mg);
+    eqr += (uint32_t)__builtin_popcountll(me);
+  }
+  __syncthreads();   // the histogram and scan buffers are free for the next row
+}
+
+// Candidate p of a row (its regions' prefix counts in pre): region i with
+// pre[i] <= p < pre[i + 1], found by walking on from i.
+__device__ __forceinline__ int64_t cand_at(const IdxArgs& a, int row, const int32_t* pre, int p, int& i) {
+  while (pre[i + 1] <= p) ++i;
+  return (int64_t)(row * a.n_kgroups + i) * a.cap + (p - pre[i]);
+}
+
+// Selection, kSelRows rows a workgroup of 1,024 threads. Each of the first kSelRows
+// waves reads its row's region counts (their prefix into LDS) and, when the row has at
+// most 64 * kWaveCand candidates and no region overflowed, selects them alone
+// (wave_select, then an emission in candidate order). Rows with more candidates take
+// the whole workgroup (select_topk on up to 32,768), rows with too few or an overflow
+// are re-scored (rescore_select), one row at a time.
+template <int H, int D>
+__global__ __launch_bounds__(kNT) void fused_select_kernel(FusedSel f) {
+  constexpr int EB = 16;   // candidates a thread holds in the workgroup selection
+  __shared__ SelShared sh;
+  __shared__ CandShared cs;
+  __shared__ int32_t pre[kSelRows][kMaxRegions + 1];
+  __shared__ int32_t need[kSelRows], nvs[kSelRows];
+  __shared__ uint32_t hist[kSelRows][256];
+  const IdxArgs& a = f.a;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nk = a.n_kgroups;
+  const uint32_t k = (uint32_t)f.k;
+  if (wid < kSelRows) {
+    const int row = blockIdx.x * kSelRows + wid;
+    int nd = 0, nv = 0;
+    uint32_t total = 0u;
+    if (row < a.n_rows) {
+      nv = f.nv[row];
+      int32_t* out = f.blocks + (int64_t)row * f.k;
+      if (f.n_valid && lane == 0) f.n_valid[row] = nv;
+      if (nv <= f.k) {
+        for (int i = lane; i < f.k; i += 64) out[i] = i < nv ? i : -1;
+      } else {
+        bool over = false;
+        for (int i0 = 0; i0 < nk; i0 += 64) {
+          const int i = i0 + lane;
+          const int c = i < nk ? a.cand_cnt[row * nk + i] : 0;
+          over |= c > a.cap;
+          const uint32_t incl = wave_incl_scan((uint32_t)(c > a.cap ? a.cap : c));
+          if (i < nk) pre[wid][i + 1] = (int32_t)(total + incl);
+          total += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        }
+        if (lane == 0) pre[wid][0] = 0;
+        nd = (__ballot(over) != 0 || total < k) ? 2 : (total > 64u * kWaveCand ? 1 : 0);
+      }
+    }
+    if (lane == 0) {
+      need[wid] = row < a.n_rows && nv > f.k ? nd : -1;
+      nvs[wid] = nv;
+    }
+    // the wave's lanes read what other lanes of it wrote to pre
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (row < a.n_rows && nv > f.k && nd == 0) {
+      int32_t* out = f.blocks + (int64_t)row * f.k;
+      uint32_t key[kWaveCand];
+      int32_t idx[kWaveCand];
+      // position e * 64 + lane, clamped to the last candidate (dropped below) so that
+      // every load is issued before any is used; its region found by walking on
+      int i = 0;
+#pragma unroll
+      for (int e = 0; e < kWaveCand; ++e) {
+        const int64_t o = cand_at(a, row, pre[wid], e * 64 + lane < (int)total ? e * 64 + lane : (int)total - 1, i);
+        key[e] = a.cand_key[o];
+        idx[e] = a.cand_idx[o];
+      }
+#pragma unroll
+      for (int e = 0; e < kWaveCand; ++e)
+        if (e * 64 + lane >= (int)total) {
+          key[e] = 0u;
+          idx[e] = -1;
+        }
+      uint32_t T, rem;
+      wave_select<kWaveCand>(key, k, 0, hist[wid], T, rem);
+      uint32_t n_eq = 0u;
+#pragma unroll
+      for (int e = 0; e < kWaveCand; ++e) n_eq += (uint32_t)__builtin_popcountll(__ballot(key[e] == T));
+      uint32_t base = 0u;
+      if (n_eq == rem) {   // every key equal to T is taken: the keys >= T, in order
+#pragma unroll
+        for (int e = 0; e < kWaveCand; ++e) {
+          const bool sel = key[e] >= T;
+          const uint64_t m = __ballot(sel);
+          const uint32_t pos =
+              base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (sel && pos < k) out[pos] = idx[e];
+          base += (uint32_t)__builtin_popcountll(m);
+        }
+      } else {
+        uint32_t eqr = 0u;
+#pragma unroll
+        for (int e = 0; e < kWaveCand; ++e) {   // candidate order: position e * 64 + lane
+          const bool is_gt = key[e] > T, is_eq = key[e] == T;
+          const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+          const uint32_t bg = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+          const uint32_t be = eqr + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+          const uint32_t pos = bg + (be < rem ? be : rem);
+          if ((is_gt || (is_eq && be < rem)) && pos < k) out[pos] = idx[e];
+          base += (uint32_t)__builtin_popcountll(mg);
+          eqr += (uint32_t)__builtin_popcountll(me);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int w = 0; w < kSelRows; ++w) {
+    const int nd = need[w];
+    if (nd <= 0) continue;
+    const int row = blockIdx.x * kSelRows + w;
+    const int nv = nvs[w];
+    int32_t* out = f.blocks + (int64_t)row * f.k;
+    const int32_t* pw = pre[w];
+    const uint32_t total = (uint32_t)pw[nk];
+    if (nd == 1 && total <= (uint32_t)(EB * kNT)) {
+      uint32_t key[EB];
+      int32_t idx[EB];
+      const int p0 = (int)threadIdx.x * EB;
+      int i = 0;
+      if (p0 < (int)total) {   // the region holding position p0: pw[i] <= p0 < pw[i + 1]
+        int hi = nk;
+        while (hi - i > 1) {
+          const int mid = (i + hi) >> 1;
+          if (pw[mid] <= p0) i = mid;
+          else hi = mid;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int p = p0 + e;
+        const int64_t o = cand_at(a, row, pw, p < (int)total ? p : (int)total - 1, i);
+        key[e] = a.cand_key[o];
+        idx[e] = a.cand_idx[o];
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+        if (p0 + e >= (int)total) {
+          key[e] = 0u;
+          idx[e] = -1;
+        }
+      select_topk<EB>(key, f.k, sh, cs, [&](int e) { return idx[e]; },
+                      [&](uint32_t pos, uint32_t, int32_t ix) { out[pos] = ix; });
+      __syncthreads();
+    } else {
+      rescore_select<H, D>(a, row, nv, f.k, out, sh);
+    }
+  }
+}
+
+template <int H, int D>
+static tf_status fused_hd(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+                          const int32_t* row_pos, const void* q, const float* w, int64_t ld, int32_t k,
+                          int32_t* blocks, int32_t* n_valid, char* ws, hipStream_t st) {
+  const FusedPlan f = fused_plan(H, n_rows, ld, k);
+  if (f.bytes == (size_t)-1) return set_error(TF_E_RANGE, "tf_indexer_topk_fused: no top-k block size fits");
+  IdxArgs a = base_args(p, v, n_rows, row_stream, row_pos, q, w);
+  if (f.direct) {
+    int32_t* nv = n_valid ? n_valid : (int32_t*)(ws + f.off_nv);
+    a.logits = (float*)(ws + f.off_smp);
+    a.ldo = ld;
+    a.kend = ld;
+    a.ncap = ld;
+    a.n_valid = nv;
+    tf_status s = launch_hd<H, D>(a, n_rows, st, kWhole);
+    if (s == TF_OK) s = launch_status("tf_indexer_topk_fused");
+    if (s != TF_OK) return s;
+    return launch_topk((const float*)(ws + f.off_smp), ld, n_rows, nv, k, blocks, f.tws ? ws + f.off_tws : nullptr,
+                       f.tws, st);
+  }
+  if ((int64_t)n_rows * f.shape.kgroups * f.cap >= 0x7fffffffLL || f.shape.kgroups > kMaxRegions)
+    return set_error(TF_E_RANGE, "tf_indexer_topk_fused: %lld key groups of %d slots for %d rows exceed one launch",
+                     (long long)f.shape.kgroups, f.cap, n_rows);
+  float* smp = (float*)(ws + f.off_smp);
+  int32_t* nvs = (int32_t*)(ws + f.off_nvs);
+  uint32_t* thr = (uint32_t*)(ws + f.off_thr);
+  int32_t* nv = (int32_t*)(ws + f.off_nv);
+  // 1. page sample
+  IdxArgs as = a;
+  as.page_step = f.step;
+  as.logits = smp;
+  as.ldo = f.S;
+  as.kend = f.S;
+  as.ncap = ld;
+  as.n_valid = nvs;
+  tf_status s = launch_hd<H, D>(as, n_rows, st, kSample, 512);
+  if (s == TF_OK) s = launch_status("tf_indexer_topk_fused");
+  if (s != TF_OK) return s;
+  // 2. thresholds
+  const unsigned g4 = (unsigned)((n_rows + 3) / 4);
+  if (f.e_thr == 32)
+    hipLaunchKernelGGL(fused_threshold_kernel<32>, dim3(g4), dim3(256), 0, st, smp, (int32_t)f.S, nvs, row_pos, ld, k,
+                       n_rows, thr);
+  else if (f.e_thr == 64)
+    hipLaunchKernelGGL(fused_threshold_kernel<64>, dim3(g4), dim3(256), 0, st, smp, (int32_t)f.S, nvs, row_pos, ld, k,
+                       n_rows, thr);
+  else if (f.S <= 8 * kNT)
+    hipLaunchKernelGGL(fused_threshold_block_kernel<8>, dim3(n_rows), dim3(kNT), 0, st, smp, (int32_t)f.S, nvs, row_pos,
+                       ld, k, thr);
+  else if (f.S <= 16 * kNT)
+    hipLaunchKernelGGL(fused_threshold_block_kernel<16>, dim3(n_rows), dim3(kNT), 0, st, smp, (int32_t)f.S, nvs,
+                       row_pos, ld, k, thr);
+  else if (f.S <= 32 * kNT)
+    hipLaunchKernelGGL(fused_threshold_block_kernel<32>, dim3(n_rows), dim3(kNT), 0, st, smp, (int32_t)f.S, nvs,
+                       row_pos, ld, k, thr);
+  else
+    return set_error(TF_E_RANGE, "tf_indexer_topk_fused: a sample of %lld keys exceeds 32,768", (long long)f.S);
+  s = launch_status("tf_indexer_topk_fused");
+  if (s != TF_OK) return s;
+  // 3. filtered scoring
+  IdxArgs af = a;
+  af.kend = ld;
+  af.ncap = ld;
+  af.n_valid = nv;
+  af.thr = thr;
+  af.cand_cnt = (int32_t*)(ws + f.off_cnt);
+  af.cand_key = (uint32_t*)(ws + f.off_ck);
+  af.cand_idx = (int32_t*)(ws + f.off_ci);
+  af.cap = f.cap;
+  s = launch_hd<H, D>(af, n_rows, st, kFilter, 1024, f.min_kpw);
+  if (s == TF_OK) s = launch_status("tf_indexer_topk_fused");
+  if (s != TF_OK) return s;
+  // 4. selection
+  af.keys_per_wg = (int32_t)f.shape.kpw;
+  af.n_kgroups = (int32_t)f.shape.kgroups;
+  FusedSel fs;
+  fs.a = af;
+  fs.nv = nv;
+  fs.n_valid = n_valid;
+  fs.k = k;
+  fs.blocks = blocks;
+  hipLaunchKernelGGL((fused_select_kernel<H, D>), dim3((unsigned)((n_rows + kSelRows - 1) / kSelRows)), dim3(kNT), 0,
+                     st, fs);
+  return launch_status("tf_indexer_topk_fused");
+}
+
+tf_status launch_indexer_topk_fused(const tf_plan* p, const DevView& v, int32_t n_rows, const int32_t* row_stream,
+                                    const int32_t* row_pos, const void* q, const float* w, int32_t n_heads,
+                                    int64_t ld, int32_t k, int32_t* blocks, int32_t* n_valid, void* ws,
+                                    hipStream_t st) {
+  char* c = (char*)ws;
+  if (p->g.index_dim == 128) {
+    if (n_heads == 16) return fused_hd<16, 128>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
+    if (n_heads == 8) return fused_hd<8, 128>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
+    return fused_hd<4, 128>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
+  }
+  if (n_heads == 16) return fused_hd<16, 64>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
+  if (n_heads == 8) return fused_hd<8, 64>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
+  return fused_hd<4, 64>(p, v, n_rows, row_stream, row_pos, q, w, ld, k, blocks, n_valid, c, st);
 }
 
 }  // namespace tf

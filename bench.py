@@ -60,8 +60,11 @@ CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
 # the one launched most often).
 ENTRIES = {
     "write": (("tf::latent_write_kernel",), "write.hip"),
-    "indexer": (("tf::indexer_rows_kernel",), "indexer.hip"),
-    "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, false>",), "indexer.hip"),
+    "indexer": (("tf::indexer_rows_kernel<16, 128, 0>",), "indexer.hip"),
+    "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, 0>",), "indexer.hip"),
+    "indexer_topk_fused": (("tf::indexer_tile_kernel<16, 128, 2, 2>", "tf::fused_threshold_kernel<4>",
+                            "tf::indexer_tile_kernel<16, 128, 2, 3>", "tf::fused_select_kernel<16, 128, 8>"),
+                           "indexer.hip"),
     "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4>"), "topk.hip"),
     "topk_prefill": (("tf::topk_row_kernel<28>",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
@@ -490,9 +493,40 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
         "quantizing_write": bench_quantizing_write(tf, pw, rs, rp, lat, rope, ks, ki, keys, reps, hbm),
         "blocked_indexer_topk": bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, blocks, reps,
                                                            idx_flop, us["indexer"] + us["topk"], mfma),
+        "fused_indexer_topk": bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, blocks, reps,
+                                                       idx_flop, us["indexer"] + us["topk"], mfma),
         "candidate_selection": bench_candidates(tf, logits, nv, pw.k, reps, hbm),
     }
     return res
+
+
+def bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, ref_blocks, reps, flop, unblocked_us, mfma):
+    """The chunk's top-512 by tf_indexer_topk_fused, which writes no logits: a page
+    sample sets each row's threshold, the filtered scoring keeps about 2k candidates a
+    row, the last kernel selects among them. Its time against the step's indexer and
+    top-k calls, its workspace against the [T, 25,000] logits buffer; the result is
+    checked equal to the step's. Its roofline counts the causal flop of one scoring
+    pass (the sample's and the threshold's work is overhead)."""
+    import numpy as np
+    import torch
+    T, ld = logits.shape
+    k = ref_blocks.shape[1]
+    got = torch.empty_like(ref_blocks)
+    ws_bytes = tf.indexer_topk_fused_workspace_bytes(T, ld, k, w.shape[1])
+    f = tf.indexer_topk_fused(plan, view, rs, rp, iq, w, ld, k, got, prepare=True)
+    f()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_blocks), "fused indexer + top-k differs from the unblocked path"
+    ev = [TimingEvent() for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        f()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+    return {"call": "tf_indexer_topk_fused", "us": round(us, 2), "unblocked_indexer_plus_topk_us": round(unblocked_us, 2),
+            "workspace_bytes": ws_bytes, "unblocked_logits_bytes": T * ld * 4, "causal_flop": flop,
+            "roofline": mfma(flop, us), "equal_to_unblocked": True}
 
 
 def bench_candidates(tf, logits, nv, k, reps, hbm, group=8, n_cand=2048):

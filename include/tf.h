@@ -12,6 +12,7 @@
  *   3. tf_topk_blocks       select the top-k pooled blocks of each row
  *                           (tf_indexer_topk runs steps 2 and 3 one key block at
  *                           a time, without the whole logits buffer;
+ *                           tf_indexer_topk_fused writes no logits at all;
  *                           tf_candidate_groups and tf_topk_in_candidates select
  *                           in two levels, candidate groups then keys);
  *   4. tf_sparse_mla_attn   absorbed-MLA softmax attention that gathers only the
@@ -236,6 +237,34 @@ tf_status tf_indexer_topk(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
                           int32_t key_block, int32_t* blocks, int32_t* n_valid, void* ws,
                           size_t ws_bytes, void* stream);
 size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t key_block);
+
+/* Fused indexer + top-k [CPM, section 2.3: only per-block top-k candidates leave the
+ * scoring, and topk(union) == topk(union of block top-k) keeps the result exact;
+ * section 1 on the [T, L] logits buffer this removes]: the blocks that
+ * tf_indexer_logits followed by tf_topk_blocks would select, bit for bit, with no
+ * logits written to memory. Each row's keys of every step-th page (about an eighth of
+ * them, at least 4,096) are scored first, and a threshold is taken among those values
+ * that about 2k of the row's keys should reach (at most the k-th largest of them). A
+ * second scoring of every key, with the same arithmetic, keeps only the keys at or
+ * above it (in key order, per key group of the launch). When at least k keys reach it,
+ * the k-th largest logit does too, so the row's top k, ties with the k-th value
+ * included, are candidates and their top k is the answer. A row with fewer than k
+ * candidates or more than its slots hold (inputs far from an even spread: many equal
+ * logits, large logits only in unsampled pages, rows much shorter than ld) is
+ * re-scored and selected exactly inside the last kernel, more slowly. Rows of at most
+ * 4,096 keys are scored whole into the workspace and selected there. Arguments, masking, n_valid, the tie rule and -1
+ * padding are those of tf_indexer_logits and tf_topk_blocks; NaN logits (missing pages)
+ * order as there. ws: 256-byte aligned device workspace of at least
+ * tf_indexer_topk_fused_workspace_bytes(n_rows, ld, k, n_heads) bytes, about
+ * n_rows x (ld / 2 + 3 k x 8) for long rows: it grows with ld at an eighth of the
+ * logits' rate. Limits: n_rows <= 65535, 1 <= k <= 2048, ld <= 2^24; four launches on
+ * `stream` (two for rows of at most 4,096 keys). */
+tf_status tf_indexer_topk_fused(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
+                                const int32_t* row_stream, const int32_t* row_pos, const void* q,
+                                const float* w, int32_t n_heads, int64_t ld, int32_t k,
+                                int32_t* blocks, int32_t* n_valid, void* ws, size_t ws_bytes,
+                                void* stream);
+size_t tf_indexer_topk_fused_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, int32_t n_heads);
 
 /* Two-level candidate selection [CPM, section 1: a layer publishes candidate
  * masks that the later low-ratio layers consume; section 2.3: its block pooling

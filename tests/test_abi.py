@@ -155,6 +155,28 @@ def test_validation_refuses_before_launch():
                              0, None) == tf.TF_OK
     # one block of logits, 4 blocks x 64 candidates x 8 bytes, n_c: per row
     assert tf.indexer_topk_workspace_bytes(8, 4096, 64, 1024) == 8 * 1024 * 4 + 8 * 4 * 64 * 8 + 32
+    # the fused indexer + top-k: k, heads, workspace size and its 256-byte alignment
+    assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 4096, 4096, fake, None, fake,
+                                   1 << 30, None) == tf.TF_E_RANGE
+    assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 8, fake, fake, fake, fake, 6, 4096, 64, fake, None, fake,
+                                   1 << 30, None) == tf.TF_E_UNSUPPORTED
+    assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 25000, 512, fake, None, fake,
+                                   1024, None) == tf.TF_E_INVAL
+    assert "workspace" in L.tf_last_error().decode()
+    assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 8, fake, fake, fake, fake, 4, 25000, 512, fake, None,
+                                   ctypes.c_void_p(0x1010), 1 << 30, None) == tf.TF_E_INVAL
+    assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 0, None, None, None, None, 4, 25000, 512, None, None, None,
+                                   0, None) == tf.TF_OK
+    # rows of at most 4,096 keys: their logits and n_c; longer rows: the sample (an
+    # eighth of the pages, at least 32 pages), thresholds, n_c and the candidate regions,
+    # less than the logits (a third of them at 2,048 rows x 25,000 keys)
+    assert tf.indexer_topk_fused_workspace_bytes(8, 4096, 64, 4) == 8 * 4096 * 4 + 256
+    # few rows of more than 4,096 keys scored whole: the top-k's blocked mode has its own
+    # workspace inside
+    assert tf.indexer_topk_fused_workspace_bytes(13, 10000, 2048, 16) >= 13 * 10000 * 4 + tf.topk_workspace_bytes(
+        13, 10000, 2048) > 13 * 10000 * 4
+    assert tf.indexer_topk_fused_workspace_bytes(8, 25000, 512, 16) < 8 * 25000 * 4
+    assert tf.indexer_topk_fused_workspace_bytes(2048, 25000, 512, 16) < 2048 * 25000 * 4 / 3
     # two-level candidate selection: group size, candidate count, bitmap capacity, workspace
     assert L.tf_candidate_groups(fake, 25000, 8, None, 0, 2048, fake, fake, 1 << 30, None) == tf.TF_E_RANGE
     assert L.tf_candidate_groups(fake, 25000, 8, None, 8, 4096, fake, fake, 1 << 30, None) == tf.TF_E_RANGE

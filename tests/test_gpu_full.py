@@ -48,6 +48,17 @@ def gpu_step(plan, view, wl, c, rows, ld, scales, q_rows=None, stream_override=N
     return logits, host(nv), host(blocks), outs
 
 
+def fused_blocks(plan, view, wl, c, rows, ld):
+    """tf_indexer_topk_fused on the same rows: (blocks, n_valid) host copies."""
+    rs, rp, iq, w, _ = query_inputs(wl, c, rows)
+    R = len(rows)
+    blocks = torch.full((R, wl.k), -7, dtype=torch.int32, device="cuda")
+    nv = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    tf.indexer_topk_fused(plan, view, rs, rp, iq, w, ld, wl.k, blocks, n_valid=nv)
+    torch.cuda.synchronize()
+    return host(blocks), host(nv)
+
+
 def test_decode_batch_full():
     """8 streams x 131,072 tokens, shuffled pages: every row against the oracle."""
     wl = decode_batch(0)
@@ -58,6 +69,9 @@ def test_decode_batch_full():
     rows, ld = wl.rows, 32768
     lg_t, nv, blk, outs = gpu_step(plan, P.view(), wl, 0, rows, ld, SCALES)
     lg = host(lg_t)
+    _log("decode batch: fused indexer + top-k equals the unblocked path")
+    fb, fnv = fused_blocks(plan, P.view(), wl, 0, rows, ld)
+    assert np.array_equal(fnv, nv) and np.array_equal(fb, blk)
     _log("decode batch: oracle logits")
     ref = ow.logits(wl, 0, rows, ld)
     check_logits(lg, ref, logits_bound(wl, 0, rows, ld), "decode batch")
@@ -82,6 +96,9 @@ def test_prefill_chunk_full():
     lg = host(lg_t)
     _log("prefill chunk: exact top-k of every row's logits")
     assert np.array_equal(blk, topk_on_values(lg, nv, wl.k))
+    _log("prefill chunk: fused indexer + top-k equals the unblocked path")
+    fb, fnv = fused_blocks(plan, P.view(), wl, 0, rows, ld)
+    assert np.array_equal(fnv, nv) and np.array_equal(fb, blk)
     rng = np.random.default_rng(7)
     sample = sorted(set([0, 1, 511, 1024, 2046, 2047] + rng.choice(2048, 10, replace=False).tolist()))
     srows = [rows[i] for i in sample]
@@ -108,6 +125,8 @@ def test_shared_prefix_decode_12_caches():
         lg_t, nv, blk, outs = gpu_step(plan, P.view(c), wl, c, rows, ld, [24.0])
         lg = host(lg_t)
         assert np.array_equal(blk, topk_on_values(lg, nv, wl.k)), f"cache {c}"
+        fb, fnv = fused_blocks(plan, P.view(c), wl, c, rows, ld)
+        assert np.array_equal(fnv, nv) and np.array_equal(fb, blk), f"fused, cache {c}"
         if c not in (0, 5, 11):
             continue
         _log(f"shared prefix: oracle, cache {c}")
