@@ -965,11 +965,26 @@ __global__ __launch_bounds__(kNT) void fused_select_kernel(FusedSel f) {
       uint32_t key[kWaveCand];
       int32_t idx[kWaveCand];
       // position e * 64 + lane, clamped to the last candidate (dropped below) so that
-      // every load is issued before any is used; its region found by walking on
+      // every load is issued before any is used; its region found by walking on from
+      // the previous one when there are few regions, else by a search of its own (64
+      // positions cross about 64 / (candidates per region) regions)
+      const int32_t* pw = pre[wid];
       int i = 0;
 #pragma unroll
       for (int e = 0; e < kWaveCand; ++e) {
-        const int64_t o = cand_at(a, row, pre[wid], e * 64 + lane < (int)total ? e * 64 + lane : (int)total - 1, i);
+        const int p = e * 64 + lane < (int)total ? e * 64 + lane : (int)total - 1;
+        int64_t o;
+        if (nk <= 16) {
+          o = cand_at(a, row, pw, p, i);
+        } else {
+          int lo = 0, hi = nk;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pw[mid] <= p) lo = mid;
+            else hi = mid;
+          }
+          o = (int64_t)(row * nk + lo) * a.cap + (p - pw[lo]);
+        }
         key[e] = a.cand_key[o];
         idx[e] = a.cand_idx[o];
       }

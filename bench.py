@@ -346,7 +346,26 @@ def bench_decode(tf, args):
                         "mean event interval"}
     indexer_scan = {"call": "tf_indexer_logits", "key_bytes": key_bytes, "us": round(avg_us["indexer"], 2),
                     "key_GBps": round(key_bytes / (avg_us["indexer"] * 1e-6) / 1e9, 1)}
-    del launches, views, pools, P0
+    # the fused indexer + top-k on the same rows (no logits written), against the pair
+    fb = torch.empty_like(blocks)
+    fused = [tf.indexer_topk_fused(plan, v, rs, rp, iq, w, ld, wl.k, fb, prepare=True) for v in views]
+    launches[0][1]()
+    launches[0][2]()
+    fused[0]()
+    torch.cuda.synchronize()
+    assert torch.equal(fb, blocks), "fused indexer + top-k differs from the pair"
+    fev = [TimingEvent() for _ in range(S + 1)]
+    fev[0].record()
+    for i in range(S):
+        fused[i % len(fused)]()
+        fev[i + 1].record()
+    torch.cuda.synchronize()
+    fus = _mean([fev[i].elapsed_time(fev[i + 1]) * 1e3 for i in range(S)])
+    fused_res = {"call": "tf_indexer_topk_fused", "us": round(fus, 2),
+                 "pair_us": round(avg_us["indexer"] + avg_us["topk"], 2), "equal_to_pair": True,
+                 "workspace_bytes": tf.indexer_topk_fused_workspace_bytes(R, ld, wl.k, wl.H),
+                 "pair_logits_bytes": R * ld * 4}
+    del launches, views, pools, P0, fused
     torch.cuda.empty_cache()
     return {"wl": wl, "rows": rows, "ld": ld, "scale": scale, "value_bytes": lat_bytes + key_bytes,
             "line": {
@@ -361,6 +380,7 @@ def bench_decode(tf, args):
                            "kernels_timing": f"mean of {S} launches per call, an event between every call"},
                 "decode_attention_latent": headline,
                 "decode_indexer_keys": indexer_scan,
+                "decode_fused_indexer_topk": fused_res,
                 "roofline": roofline,
                 "kernels": kern,
                 "wall_s_timed": round(wall, 4)}}
