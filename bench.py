@@ -59,13 +59,15 @@ CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
 # they are separate entries; the latent write is one kernel in both (its decode grid is
 # the one launched most often).
 ENTRIES = {
-    "write": (("tf::latent_write_kernel",), "write.hip"),
+    "write": (("tf::latent_write_kernel [grid 768]",), "write.hip"),
     "indexer": (("tf::indexer_rows_kernel<16, 128, 0>",), "indexer.hip"),
     "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, 0>",), "indexer.hip"),
-    "indexer_topk_fused": (("tf::indexer_tile_kernel<16, 128, 2, 2>", "tf::fused_threshold_kernel<4>",
-                            "tf::indexer_tile_kernel<16, 128, 2, 3>", "tf::fused_select_kernel<16, 128, 8>"),
+    # the prefill chunk's launches (its threshold and selection kernels by grid: the decode
+    # batch's comparison launches the same instances at other sizes)
+    "indexer_topk_fused": (("tf::indexer_tile_kernel<16, 128, 2, 2>", "tf::fused_threshold_kernel<32> [grid 131072]",
+                            "tf::indexer_tile_kernel<16, 128, 2, 3>", "tf::fused_select_kernel<16, 128> [grid 262144]"),
                            "indexer.hip"),
-    "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4>"), "topk.hip"),
+    "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4> [grid 8192]"), "topk.hip"),
     "topk_prefill": (("tf::topk_row_kernel<28>",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
     "attention_prefill": (("tf::attn_kernel_w32",), "attention.hip"),
@@ -1095,6 +1097,8 @@ def summarize_trace(db, label, command, bench_json=None):
                 ev[e] = b["prefill_step"]["calls"][call]["us"]
         if b.get("dense_pass"):
             ev["attention_dense"] = b["dense_pass"]["us"]
+        if b.get("prefill_step", {}).get("fused_indexer_topk"):
+            ev["indexer_topk_fused"] = b["prefill_step"]["fused_indexer_topk"]["us"]
         for e, us in ev.items():
             k = sum(a for _, _, a in per_entry.get(e, []))
             lines.append(f"{e:16s} events {us:9.2f} us   kernels {k:9.2f} us   ratio {us / k if k else 0:.3f}")
@@ -1151,17 +1155,22 @@ def summarize_counters(db, label, command, prefixes):
 
 
 def _pmc(db, counter):
-    """kernel -> counter values per dispatch, for the grid size launched most often
-    (the timed launches, not the pool population's)."""
+    """(kernel, grid size) -> counter values per dispatch."""
     c = sqlite3.connect(db)
     by = {}
     for name, g, v in c.execute("select p.name, k.grid_x * k.grid_y * k.grid_z, p.counter_value from pmc_events p "
                                 "join kernels k on p.dispatch_id = k.dispatch_id where p.counter_name = ?",
                                 (counter,)):
-        by.setdefault(_short(name), {}).setdefault(g, []).append(float(v))
-    counts = [len(v) for n, gs in by.items() if _entry_of(n) for v in gs.values()]
-    timed = max(set(counts), key=counts.count)       # the decode step's launch count
-    return {n: next((v for v in gs.values() if len(v) == timed), max(gs.values(), key=len)) for n, gs in by.items()}
+        by.setdefault((_short(name), g), []).append(float(v))
+    return by
+
+
+def _pick(by, pattern):
+    """The (kernel, grid) of a listed kernel name: the grid it pins (" [grid N]"), else the
+    grid launched most often."""
+    base, _, g = pattern.partition(" [grid ")
+    cands = [kg for kg in by if _matches(kg[0], base) and (not g or kg[1] == int(g.rstrip("]")))]
+    return max(cands, key=lambda kg: len(by[kg])) if cands else None
 
 
 def summarize_pmc(fetch_db, write_db, command, traffic_file=TRAFFIC_FILE):
@@ -1169,25 +1178,28 @@ def summarize_pmc(fetch_db, write_db, command, traffic_file=TRAFFIC_FILE):
     pass (KiB per dispatch), each scaled by what the same counter reads for the
     calibration stream (CAL_BYTES read and CAL_BYTES written by one torch.neg)."""
     fetch, write = _pmc(fetch_db, "FETCH_SIZE"), _pmc(write_db, "WRITE_SIZE")
-    cal = [k for k in fetch if CAL_KERNEL in k]
+    cal = [kg for kg in fetch if CAL_KERNEL in kg[0]]
     if cal:
         cf = CAL_BYTES / (fetch[cal[0]][0] * 1024.0)
-        cw = CAL_BYTES / (write[[k for k in write if CAL_KERNEL in k][0]][0] * 1024.0)
-        calib = {"kernel": cal[0], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES}
+        cw = CAL_BYTES / (write[[kg for kg in write if CAL_KERNEL in kg[0]][0]][0] * 1024.0)
+        calib = {"kernel": cal[0][0], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES}
     else:   # a pass over a leg without the stream: the scales of the decode pass's file
         assert traffic_file != TRAFFIC_FILE, "the calibration kernel is missing from the FETCH_SIZE pass"
         prev = json.load(open(os.path.join(PROFILES, TRAFFIC_FILE)))["calibration"]
         cf, cw = prev["fetch_scale"], prev["write_scale"]
         calib = {"from": TRAFFIC_FILE, "kernel": prev["kernel"], "bytes_read": CAL_BYTES, "bytes_written": CAL_BYTES}
     entries = {}
-    for n in fetch:
-        e = _entry_of(n)
-        if e is None:
-            continue
-        f_kib = sum(fetch[n]) / len(fetch[n])
-        w_kib = sum(write.get(n, [0.0])) / max(1, len(write.get(n, [])))
-        d = entries.setdefault(e, {"kernels": {}, "source_sha256_16": source_hash(ENTRIES[e][1])})
-        d["kernels"][n] = {"fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1), "dispatches": len(fetch[n])}
+    for e, (patterns, src) in ENTRIES.items():
+        for p in patterns:
+            kg = _pick(fetch, p)
+            if kg is None:
+                continue
+            f_kib = sum(fetch[kg]) / len(fetch[kg])
+            w = write.get(kg, [0.0])
+            w_kib = sum(w) / max(1, len(w))
+            d = entries.setdefault(e, {"kernels": {}, "source_sha256_16": source_hash(src)})
+            d["kernels"][f"{kg[0]} [grid {kg[1]}]"] = {"fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+                                                       "dispatches": len(fetch[kg])}
     for e, d in entries.items():
         fb = sum(k["fetch_kib"] for k in d["kernels"].values()) * 1024.0 * cf
         wb = sum(k["write_kib"] for k in d["kernels"].values()) * 1024.0 * cw
