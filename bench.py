@@ -516,19 +516,22 @@ def bench_prefill_step(tf, pw, plan, PP, rs, rp, iq, w, logits, nv, reps):
         "blocked_indexer_topk": bench_blocked_indexer_topk(tf, pw, plan, view, rs, rp, iq, w, logits, blocks, reps,
                                                            idx_flop, us["indexer"] + us["topk"], mfma),
         "fused_indexer_topk": bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, blocks, reps,
-                                                       idx_flop, us["indexer"] + us["topk"], mfma),
+                                                       idx_flop, us["indexer"] + us["topk"], mfma, dict(calls)),
         "candidate_selection": bench_candidates(tf, logits, nv, pw.k, reps, hbm),
     }
     return res
 
 
-def bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, ref_blocks, reps, flop, unblocked_us, mfma):
+def bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, ref_blocks, reps, flop, unblocked_us, mfma,
+                             step_calls):
     """The chunk's top-512 by tf_indexer_topk_fused, which writes no logits: a page
     sample sets each row's threshold, the filtered scoring keeps about 2k candidates a
-    row, the last kernel selects among them. Its time against the step's indexer and
-    top-k calls, its workspace against the [T, 25,000] logits buffer; the result is
-    checked equal to the step's. Its roofline counts the causal flop of one scoring
-    pass (the sample's and the threshold's work is overhead)."""
+    row, the last kernel selects among them. Timed inside the step, in place of the
+    indexer and top-k calls (write, fused, attention, an event between calls), as the
+    pair is: back-to-back launches of one MFMA-bound kernel run slower than the same
+    launches between the step's other calls. Its workspace against the [T, 25,000]
+    logits buffer; the result is checked equal to the step's. The roofline counts the
+    causal flop of one scoring pass (the sample's work is overhead)."""
     import numpy as np
     import torch
     T, ld = logits.shape
@@ -539,14 +542,24 @@ def bench_fused_indexer_topk(tf, plan, view, rs, rp, iq, w, logits, ref_blocks, 
     f()
     torch.cuda.synchronize()
     assert torch.equal(got, ref_blocks), "fused indexer + top-k differs from the unblocked path"
-    ev = [TimingEvent() for _ in range(reps + 1)]
-    ev[0].record()
+    calls = [step_calls["write"], f, step_calls["attention"]]
+    ev = [[TimingEvent() for _ in range(len(calls) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        for c, g in enumerate(calls):
+            g()
+            ev[i][c + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(reps)])) * 1e3
+    b2b = TimingEvent(), TimingEvent()
+    b2b[0].record()
     for i in range(reps):
         f()
-        ev[i + 1].record()
+    b2b[1].record()
     torch.cuda.synchronize()
-    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
     return {"call": "tf_indexer_topk_fused", "us": round(us, 2), "unblocked_indexer_plus_topk_us": round(unblocked_us, 2),
+            "us_back_to_back": round(b2b[0].elapsed_time(b2b[1]) * 1e3 / reps, 2),
+            "timing": "in the step in place of the indexer and top-k calls, as they are timed",
             "workspace_bytes": ws_bytes, "unblocked_logits_bytes": T * ld * 4, "causal_flop": flop,
             "roofline": mfma(flop, us), "equal_to_unblocked": True}
 
