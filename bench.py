@@ -896,6 +896,7 @@ def bench_adaptive_prefill(tf):
         b["attention_us"] = round(b["attention_us"], 1)
         b["tok_per_s"] = round(b["tokens"] / (b["us"] * 1e-6), 1)
     calls_total = {n: round(sum(c[j] for c in call_us), 1) for j, n in enumerate(names)}
+    fused = adaptive_fused_pass(tf, plan, view, wl, sched, chunk_calls, rs, rp, iq, w, nv, blocks)
     # snapshot of the first 262,144 rows of stream 0 into stream 1's pages
     at = 262144
     src = torch.tensor([0], dtype=torch.int32, device="cuda")
@@ -926,10 +927,51 @@ def bench_adaptive_prefill(tf):
            "snapshot": {"call": "tf_snapshot_copy", "at": at, "bytes_each_way": snap_bytes, "us": round(snap_us, 2),
                         "reps": sreps, "GBps_read_plus_written": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+           "fused_indexer_topk_pass": fused,
            "timing": "an event between every call; inputs generated into HBM before the first chunk"}
     del P, lat, sc, rope, keys, q, iq, w, logbuf, out
     torch.cuda.empty_cache()
     return res
+
+
+def adaptive_fused_pass(tf, plan, view, wl, sched, chunk_calls, rs, rp, iq, w, nv, blocks):
+    """The same 464 chunks with tf_indexer_topk_fused in place of the indexer and top-k
+    calls (no logits written): first every 16th chunk's blocks checked equal to the
+    pair's, then the whole prompt timed as the pair is (an event between calls)."""
+    import torch
+    ws = torch.empty(max(256, max(tf.indexer_topk_fused_workspace_bytes(T, (L + T - 1) // 4 + 1, wl.k, wl.H)
+                                  for L, T in sched)), dtype=torch.uint8, device="cuda")
+    fb = torch.empty_like(blocks)
+
+    def fused(L, T):
+        ld = (L + T - 1) // 4 + 1
+        return lambda: tf.indexer_topk_fused(plan, view, rs[L:L + T], rp[L:L + T], iq[L:L + T], w[L:L + T], ld,
+                                             wl.k, fb[:T], ws=ws)
+    checked = 0
+    for L, T in sched[::16]:
+        c = chunk_calls(L, T)
+        c[1]()
+        c[2]()
+        fused(L, T)()
+        torch.cuda.synchronize()
+        assert torch.equal(fb[:T], blocks[:T]), f"fused blocks differ at chunk L={L}"
+        checked += 1
+    ev = [[TimingEvent() for _ in range(4)] for _ in sched]
+    for i, (L, T) in enumerate(sched):
+        c = chunk_calls(L, T)
+        ev[i][0].record()
+        for j, f in enumerate((c[0], fused(L, T), c[3])):
+            f()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    call_us = [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for j in range(3)] for i in range(len(sched))]
+    total = ev[0][0].elapsed_time(ev[-1][3]) * 1e3
+    n_tok = sum(T for _, T in sched)
+    del ws
+    return {"total_us": round(total, 1), "tok_per_s": round(n_tok / (total * 1e-6), 1),
+            "calls_total_us": {n: round(sum(c[j] for c in call_us), 1)
+                               for j, n in enumerate(("write", "indexer_topk_fused", "attention"))},
+            "chunks_checked_equal": checked}
 
 
 def cpu_baseline(wl, rows, ld, scale, seconds, step_bytes):
