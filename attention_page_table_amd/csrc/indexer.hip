@@ -711,7 +711,7 @@ static FusedPlan fused_plan(int H, int32_t n_rows, int64_t ld, int32_t k) {
   f.min_kpw = (mk + 127) / 128 * 128;
   f.shape = idx_shape(H, n_rows, ld, 1024, f.min_kpw);
   // slots: twice the passes expected of a row of ld keys (kpw * 2k / ld) plus 32, at
-  // most kpw (the sample's threshold varies a row's candidates by about a quarter)
+  // most kpw (the sample's threshold moves a row's candidates by up to about a half)
   int64_t cap = (int64_t)(2.0 * (double)f.shape.kpw * 2.0 * k / (double)ld) + 32;
   cap = (cap + 3) / 4 * 4;
   f.cap = (int32_t)(cap < f.shape.kpw ? cap : f.shape.kpw);

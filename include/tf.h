@@ -242,8 +242,8 @@ size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, in
  * scoring, and topk(union) == topk(union of block top-k) keeps the result exact;
  * section 1 on the [T, L] logits buffer this removes]: the blocks that
  * tf_indexer_logits followed by tf_topk_blocks would select, bit for bit, with no
- * logits written to memory. Each row's keys of every step-th page (about an eighth of
- * them, at least 4,096) are scored first, and a threshold is taken among those values
+ * logits written to memory. Each row's keys of every step-th page (about a sixteenth
+ * of them, at least 2,048) are scored first, and a threshold is taken among those values
  * that about 2k of the row's keys should reach (at most the k-th largest of them). A
  * second scoring of every key, with the same arithmetic, keeps only the keys at or
  * above it (in key order, per key group of the launch). When at least k keys reach it,
@@ -256,8 +256,8 @@ size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, in
  * padding are those of tf_indexer_logits and tf_topk_blocks; NaN logits (missing pages)
  * order as there. ws: 256-byte aligned device workspace of at least
  * tf_indexer_topk_fused_workspace_bytes(n_rows, ld, k, n_heads) bytes, about
- * n_rows x (ld / 2 + 3 k x 8) for long rows: it grows with ld at an eighth of the
- * logits' rate. Limits: n_rows <= 65535, 1 <= k <= 2048, ld <= 2^24; four launches on
+ * n_rows x (ld / 4 + 4 k x 8) for long rows: it grows with ld at a sixteenth of
+ * the logits' rate. Limits: n_rows <= 65535, 1 <= k <= 2048, ld <= 2^24; four launches on
  * `stream` (two for rows of at most 4,096 keys). */
 tf_status tf_indexer_topk_fused(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
                                 const int32_t* row_stream, const int32_t* row_pos, const void* q,

@@ -168,7 +168,7 @@ def test_validation_refuses_before_launch():
     assert L.tf_indexer_topk_fused(ctypes.byref(p), v, 0, None, None, None, None, 4, 25000, 512, None, None, None,
                                    0, None) == tf.TF_OK
     # rows of at most 4,096 keys: their logits and n_c; longer rows: the sample (an
-    # eighth of the pages, at least 32 pages), thresholds, n_c and the candidate regions,
+    # sixteenth of the pages, at least 16 pages), thresholds, n_c and the candidate regions,
     # less than the logits (a third of them at 2,048 rows x 25,000 keys)
     assert tf.indexer_topk_fused_workspace_bytes(8, 4096, 64, 4) == 8 * 4096 * 4 + 256
     # few rows of more than 4,096 keys scored whole: the top-k's blocked mode has its own
