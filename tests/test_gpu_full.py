@@ -146,7 +146,8 @@ def test_shared_prefix_decode_12_caches():
 
 def test_adaptive_prefill_fp8_snapshot_resume():
     """390,000-token prompt in fp8 rows, chunk(L) = clamp(round_down_256(2e8 / L), 256, 2048);
-    sampled rows of several chunks against the oracle; then the first 262,144 rows are
+    sampled rows of several chunks against the oracle, and the fused indexer + top-k's
+    blocks equal to the pair's on every 29th chunk; then the first 262,144 rows are
     snapshot into fresh pages, one 2,048-token chunk is resumed there, and it equals
     the same rows of the fresh run bit for bit."""
     wl = adaptive_prefill(0)
@@ -165,6 +166,9 @@ def test_adaptive_prefill_fp8_snapshot_resume():
         rows = [(0, t) for t in range(L, L + T)]
         ld = (L + T - 1) // 4 + 1
         lg_t, nv, blk, outs = gpu_step(plan, view, wl, 0, rows, ld, [24.0])
+        if n_chunks % 29 == 0 or n_chunks in (47, 48, 463):   # every chunk size, short and long prefixes
+            fb, fnv = fused_blocks(plan, view, wl, 0, rows, ld)
+            assert np.array_equal(fnv, nv) and np.array_equal(fb, blk), f"fused, chunk at {L}"
         if n_chunks in (0, 1, 47, 48, 100, 200, 463) or L + T == N:
             sel = sorted(set([0, T - 1] + rng.choice(T, 2, replace=False).tolist()))
             checks.append((L, T, ld, [rows[i] for i in sel], host(lg_t)[sel], nv[sel], blk[sel],
