@@ -25,7 +25,9 @@ Reported:
   whole-buffer calls, and its two-level candidate selection (top-2,048 groups of 8
   keys, then top-512 inside them);
 * the dense pass (no indexer or top-k) over a 2,048-row chunk at L = 4,096;
-* the oracle timed on the host cores on a bounded sample of the same step.
+* the oracle timed on the host cores on a bounded sample of the same step;
+* the box's achievable rates in the same run (a 1 GiB streaming copy, an 8,192^3
+  bf16 GEMM), and every fraction of a nominal peak also against them.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 20]
 
@@ -141,7 +143,7 @@ def load_traffic(entry, traffic_file=TRAFFIC_FILE):
     return e.get("hbm_bytes_per_launch")
 
 
-LEGS = ("decode", "prefill", "dense", "c4", "c5", "cpu")
+LEGS = ("decode", "prefill", "dense", "c4", "c5", "cpu", "peaks")
 
 
 def main():
@@ -218,7 +220,73 @@ def main():
         cpu = cpu_baseline(dec["wl"], dec["rows"], dec["ld"], dec["scale"], args.cpu_seconds, dec["value_bytes"])
         cpu["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)
         line["cpu_baseline"] = cpu
+    if "peaks" in legs:
+        line["achievable_peaks"] = measure_peaks(torch)
+        annotate_achievable(line, line["achievable_peaks"])
     print(json.dumps(line), flush=True)
+
+
+def measure_peaks(torch, reps=20):
+    """The box's achievable rates, measured in the same run after the legs (warm clocks):
+    a streaming copy (torch.neg over 1 GiB of float32: 1 GiB read and 1 GiB written) and
+    an 8,192^3 bf16 GEMM (torch.mm, both operands contiguous). Median of `reps` event
+    intervals, each holding one launch."""
+    torch.cuda.empty_cache()
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [TimingEvent() for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return _median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])   # ms
+
+    copy_ms = timed(lambda: torch.neg(src, out=dst))
+    gemm_ms = timed(lambda: torch.mm(a, b, out=c))
+    copy_gbs = 2 * CAL_BYTES / (copy_ms * 1e-3) / 1e9
+    gemm_tfl = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(copy_gbs, 1), "copy": "torch.neg over 1 GiB of float32 (bytes read + written)",
+            "copy_frac_of_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "gemm_bf16_TFLOPs": round(gemm_tfl, 1), "gemm": "torch.mm, bf16, 8192 x 8192 x 8192",
+            "gemm_frac_of_mfma_peak": round(gemm_tfl / MFMA_BF16_PEAK_TFLOPS, 4), "reps": reps}
+
+
+def annotate_achievable(obj, peaks):
+    """Beside every fraction of a nominal peak, the same figure against the measured one:
+    roofline objects get `achievable` and `frac_achievable`; fields frac_hbm* and
+    frac_mfma* get a twin with the suffix _achievable."""
+    if isinstance(obj, list):
+        for v in obj:
+            annotate_achievable(v, peaks)
+        return
+    if not isinstance(obj, dict) or obj is peaks:
+        return
+    hbm, mfma = peaks["copy_GBps"], peaks["gemm_bf16_TFLOPs"]
+    if {"bound", "achieved", "peak", "unit"} <= obj.keys():
+        ach = hbm if obj["unit"] == "GB/s" else (mfma if obj["unit"] == "TFLOP/s" else None)
+        if ach:
+            obj["achievable"] = ach
+            obj["frac_achievable"] = round(obj["achieved"] / ach, 4)
+    for key in list(obj.keys()):
+        if key.startswith("frac_hbm") and isinstance(obj[key], (int, float)):
+            obj[key + "_achievable"] = round(obj[key] * HBM_PEAK_GBS / hbm, 4)
+        elif key.startswith("frac_mfma") and isinstance(obj[key], (int, float)):
+            obj[key + "_achievable"] = round(obj[key] * MFMA_BF16_PEAK_TFLOPS / mfma, 4)
+    for v in list(obj.values()):
+        annotate_achievable(v, peaks)
 
 
 def _mean(xs):
@@ -806,7 +874,8 @@ def bench_adaptive_prefill(tf):
     applies): per chunk, write its rows and keys, score its rows against every visible
     key, top-512, attention with 32 heads. All inputs are generated into HBM first; an
     event between every call. Then the snapshot of the first 262,144 rows (every plane
-    and the keys [0, 65,536)) into another stream's pages, timed alone."""
+    and the keys [0, 65,536)) into another stream's pages, timed alone: each copy after
+    1 GiB written (the Infinity Cache cold for the source), and back to back."""
     import numpy as np
     import torch
 
@@ -905,13 +974,28 @@ def bench_adaptive_prefill(tf):
     f()
     torch.cuda.synchronize()
     sreps = 10
+    # cold (the figure): 1 GiB written before each copy, outside its events, so that no
+    # source line is in the 256 MB Infinity Cache and that cache is full of dirty lines
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(sreps):
+        flush.fill_(float(i))
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    # hot: back to back, the source largely in the Infinity Cache from the copy before
     se = [TimingEvent() for _ in range(sreps + 1)]
     se[0].record()
     for i in range(sreps):
         f()
         se[i + 1].record()
     torch.cuda.synchronize()
-    snap_us = _mean([se[i].elapsed_time(se[i + 1]) * 1e3 for i in range(sreps)])
+    snap_hot_us = _mean([se[i].elapsed_time(se[i + 1]) * 1e3 for i in range(sreps)])
+    snap_us = _median(cold)
     snap_bytes = at * (plan.lat_row_bytes + 4 + plan.rope_row_bytes) + (at // 4) * plan.pkey_row_bytes
     res = {"workload": wl.name, "tokens": N, "chunks": len(sched), "total_us": round(total_us, 1),
            "tok_per_s": round(N / (total_us * 1e-6), 1), "calls_total_us": calls_total,
@@ -926,7 +1010,9 @@ def bench_adaptive_prefill(tf):
                                             / MFMA_BF16_PEAK_TFLOPS, 4)},
            "snapshot": {"call": "tf_snapshot_copy", "at": at, "bytes_each_way": snap_bytes, "us": round(snap_us, 2),
                         "reps": sreps, "GBps_read_plus_written": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9, 1),
-                        "frac_hbm": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "frac_hbm": round(2 * snap_bytes / (snap_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "timing": "median of copies each after 1 GiB written (Infinity Cache cold and dirty)",
+                        "us_back_to_back": round(snap_hot_us, 2)},
            "fused_indexer_topk_pass": fused,
            "timing": "an event between every call; inputs generated into HBM before the first chunk"}
     del P, lat, sc, rope, keys, q, iq, w, logbuf, out
