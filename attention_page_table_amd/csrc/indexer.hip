@@ -659,9 +659,13 @@ tf_status launch_indexer(const tf_plan* p, const DevView& v, int32_t n_rows, con
 //    overflowed region (more passes than slots) is re-scored inside the selection kernel
 //    instead: three radix passes, a count and an emission, each scoring its keys anew.
 // Rows of at most max(4,096, 8k) keys are scored whole into the workspace and selected
-// there (the candidates would be a large share of the keys anyway).
+// there (the candidates would be a large share of the keys anyway), and so are calls of
+// fewer than 64 rows of at most kFewRowsKeys keys: a decode batch's logits are small
+// (8 rows x 32,768 keys: 1 MB), and its four dependent launches on few rows took 58 us
+// against 33 us for the scoring and top-k kernels of the unfused pair.
 
 constexpr int kMaxRegions = 512;   // key groups of the filtered pass
+constexpr int64_t kFewRowsKeys = 1 << 18;   // longest rows a call of fewer than 64 scores whole
 constexpr int kSelRows = 8;        // rows of a selection workgroup, one a wave
 constexpr int kWaveCand = 24;      // candidates a lane holds in the one-wave selection
 
@@ -686,7 +690,7 @@ static FusedPlan fused_plan(int H, int32_t n_rows, int64_t ld, int32_t k) {
     return o;
   };
   const int64_t pages = (ld + kKeysPerPage - 1) / kKeysPerPage;
-  if (ld <= 4096 || ld <= 8 * (int64_t)k) {
+  if (ld <= 4096 || ld <= 8 * (int64_t)k || (n_rows < 64 && ld <= kFewRowsKeys)) {
     f.direct = true;
     f.step = 1;
     f.S = ld;

@@ -252,13 +252,17 @@ size_t tf_indexer_topk_workspace_bytes(int32_t n_rows, int64_t ld, int32_t k, in
  * candidates or more than its slots hold (inputs far from an even spread: many equal
  * logits, large logits only in unsampled pages, rows much shorter than ld) is
  * re-scored and selected exactly inside the last kernel, more slowly. Rows of at most
- * 4,096 keys are scored whole into the workspace and selected there. Arguments, masking, n_valid, the tie rule and -1
+ * max(4,096, 8k) keys, and calls of fewer than 64 rows of at most 262,144 keys (decode
+ * batches: their logits are small, and the sample and threshold launches would cost
+ * more than the buffer saves), are scored whole into the workspace and selected there,
+ * by the kernels of the unfused pair. Arguments, masking, n_valid, the tie rule and -1
  * padding are those of tf_indexer_logits and tf_topk_blocks; NaN logits (missing pages)
  * order as there. ws: 256-byte aligned device workspace of at least
  * tf_indexer_topk_fused_workspace_bytes(n_rows, ld, k, n_heads) bytes, about
  * n_rows x (ld / 4 + 4 k x 8) for long rows: it grows with ld at a sixteenth of
- * the logits' rate. Limits: n_rows <= 65535, 1 <= k <= 2048, ld <= 2^24; four launches on
- * `stream` (two for rows of at most 4,096 keys). */
+ * the logits' rate (n_rows x ld x 4 and the top-k's own workspace when scored whole).
+ * Limits: n_rows <= 65535, 1 <= k <= 2048, ld <= 2^24; four launches on `stream` (two
+ * or three when scored whole). */
 tf_status tf_indexer_topk_fused(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
                                 const int32_t* row_stream, const int32_t* row_pos, const void* q,
                                 const float* w, int32_t n_heads, int64_t ld, int32_t k,

@@ -175,7 +175,11 @@ def test_validation_refuses_before_launch():
     # workspace inside
     assert tf.indexer_topk_fused_workspace_bytes(13, 10000, 2048, 16) >= 13 * 10000 * 4 + tf.topk_workspace_bytes(
         13, 10000, 2048) > 13 * 10000 * 4
-    assert tf.indexer_topk_fused_workspace_bytes(8, 25000, 512, 16) < 8 * 25000 * 4
+    # fewer than 64 rows of at most 262,144 keys are scored whole too; more rows, or
+    # longer ones, take the sample and the filtered pass
+    assert tf.indexer_topk_fused_workspace_bytes(8, 25000, 512, 16) >= 8 * 25000 * 4
+    assert tf.indexer_topk_fused_workspace_bytes(8, 300000, 512, 16) < 8 * 300000 * 4
+    assert tf.indexer_topk_fused_workspace_bytes(64, 25000, 512, 16) < 64 * 25000 * 4
     assert tf.indexer_topk_fused_workspace_bytes(2048, 25000, 512, 16) < 2048 * 25000 * 4 / 3
     # two-level candidate selection: group size, candidate count, bitmap capacity, workspace
     assert L.tf_candidate_groups(fake, 25000, 8, None, 0, 2048, fake, fake, 1 << 30, None) == tf.TF_E_RANGE

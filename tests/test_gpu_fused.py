@@ -4,15 +4,16 @@ tf_topk_blocks, bit for bit, through the C ABI.
 
 Two streams of 40,000 and 36,000 tokens (10,000 and 9,000 pooled keys, so the page
 sample and the filtered pass run) reach every kernel path: the row kernel (fewer than
-64 rows), the tile kernel (256 rows of one stream) and its per-row fallback (rows
-alternating between the streams). Rows that see at most k keys, a row before its
+64 rows; with ld = 300,000, since calls of fewer than 64 rows of at most 262,144 keys
+are scored whole), the tile kernel (256 rows of one stream) and its per-row fallback
+(rows alternating between the streams). Rows that see at most k keys, a row before its
 stream's start and ragged lengths are included; so are inputs that overflow the
 candidate regions and take the re-scoring path: rows whose logits all tie (zero
 queries) and keys scaled up in all but every third page, so that a page sample sees
 mostly small logits. k = 1024 takes the workgroup selection (about 2,048 candidates a
-row); k = 2048 and short rows (at most max(4,096, 8k) keys) take the direct path, whose
-top-k runs its blocked mode on few rows. Sampled rows are also checked against the
-oracle's logits."""
+row); k = 2048, short rows (at most max(4,096, 8k) keys) and few rows at ld = 10,000
+take the direct path, whose top-k runs its blocked mode on few rows. Sampled rows are
+also checked against the oracle's logits."""
 import dataclasses
 
 import numpy as np
@@ -64,6 +65,10 @@ ROWS = {
     "tile": [(0, t) for t in range(39744, 40000)],
     "mixed": [(i % 2, 20000 + 61 * i) for i in range(128)],
 }
+ROWS["rows_direct"] = ROWS["rows"]
+# the logits' row length per case: 13 rows take the filtered row kernel only past
+# 262,144 keys (keys past a row's visible count are -inf)
+LD = {"rows": 300000, "rows_direct": 10000, "tile": 10000, "mixed": 10000}
 
 
 def _reference(plan, P, rs, rp, iq, w, ld, k):
@@ -84,7 +89,7 @@ def _fused(plan, P, rs, rp, iq, w, ld, k, ws=None):
     return got, nv
 
 
-@pytest.mark.parametrize("path", ["rows", "tile", "mixed"])
+@pytest.mark.parametrize("path", ["rows", "rows_direct", "tile", "mixed"])
 @pytest.mark.parametrize("H,Dk,k", [(16, 128, 512), (16, 128, 64), (16, 128, 1024), (16, 128, 2048), (8, 128, 512),
                                     (4, 64, 512), (16, 64, 200)])
 def test_fused_equals_unblocked(H, Dk, k, path):
@@ -92,9 +97,9 @@ def test_fused_equals_unblocked(H, Dk, k, path):
     wl0, plan, P = _pool(Dk)
     wl = dataclasses.replace(wl0, H=H, w_d=float(H))
     rows = ROWS[path]
-    ld = 10000
+    ld = LD[path]
     rs, rp, iq, w, _ = query_inputs(wl, 0, [(b, max(t, 0)) for b, t in rows])
-    if path == "rows":
+    if path.startswith("rows"):
         rp[-1] = -1
     ref, nv = _reference(plan, P, rs, rp, iq, w, ld, k)
     got, nv2 = _fused(plan, P, rs, rp, iq, w, ld, k)
@@ -104,6 +109,9 @@ def test_fused_equals_unblocked(H, Dk, k, path):
 
 
 def test_fused_against_oracle():
+    """20 rows (decode rows and every 37th tile row) at ld = 10,000: the direct path
+    against the oracle's logits (the filtered paths are checked bit for bit against the
+    unblocked pair, which is checked against the oracle)."""
     _log("fused indexer + top-k: oracle on decode and tile rows")
     wl, plan, P = _pool(128)
     rows = ROWS["rows"][:-1] + ROWS["tile"][::37]
@@ -124,7 +132,7 @@ def test_fused_tied_rows_take_the_rescoring_path(path):
     _log(f"fused indexer + top-k: tied rows ({path})")
     wl, plan, P = _pool(128)
     rows = ROWS[path]
-    ld = 10000
+    ld = LD[path]
     rs, rp, iq, w, _ = query_inputs(wl, 0, [(b, max(t, 0)) for b, t in rows])
     if path == "rows":
         rp[-1] = -1
@@ -159,9 +167,11 @@ def test_fused_keys_large_outside_the_sample():
         seg = pool16[o:o + 128 * plan.pkey_row_bytes // 2]
         exp = (seg >> 7) & 0xFF
         seg.copy_(torch.where((exp > 0) & (exp < 0xFD), seg + 0x100, seg))
-    ld = 10000
-    for rows in (ROWS["rows"][:-1], ROWS["tile"]):
-        rs, rp, iq, w, _ = query_inputs(wl, 0, rows)
+    for path in ("rows", "tile"):
+        rows, ld = ROWS[path], LD[path]
+        rs, rp, iq, w, _ = query_inputs(wl, 0, [(b, max(t, 0)) for b, t in rows])
+        if path == "rows":
+            rp[-1] = -1
         ref, nv = _reference(plan, P, rs, rp, iq, w, ld, wl.k)
         got, nv2 = _fused(plan, P, rs, rp, iq, w, ld, wl.k)
         torch.cuda.synchronize()
