@@ -1211,7 +1211,9 @@ def summarize_trace(db, label, command, bench_json=None):
     for n, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{n[:60]:60s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} {max(v):10.2f} "
                      f"{sum(v):12.1f}")
-        e = _entry_of(n)
+        # entries may name a kernel with its grid: match on the name tagged with its grid
+        # even where it was launched at one size only (and so printed without the tag)
+        e = _entry_of(n if " [grid" in n else f"{n} [grid {next(iter(grids[n]))}]")
         if e is not None:
             per_entry.setdefault(e, []).append((n, len(v), sum(v) / len(v)))
     # an entry's kernel launched at several sizes: keep the size launched most often (the timed one)
