@@ -362,7 +362,10 @@ size_t tf_attn_workspace_bytes(int32_t n_rows, int32_t n_heads, int32_t k);
  * stream src_stream[i] of `src` to stream dst_stream[i] of `dst` (two views of
  * the same geometry; their `cache` fields are ignored). Rows at or past `at`
  * are neither read nor written. `at` must be a multiple of 4 and fit both
- * tables' strides; the stream index arrays are device int32. */
+ * tables' strides; the stream index arrays are device int32. A page the call both
+ * reads and writes must sit at the same page index in both tables (a page the two
+ * tables share copies onto itself); any other overlap of read and written pages
+ * gives undefined bytes. The copy streams past the caches (non-temporal). */
 tf_status tf_snapshot_copy(const tf_plan* p, tf_kv_view src, tf_kv_view dst, int32_t n_streams,
                            const int32_t* src_stream, const int32_t* dst_stream, int64_t at,
                            void* stream);
