@@ -789,7 +789,7 @@ __global__ __launch_bounds__(kNT) void fused_threshold_block_kernel(const float*
     return;
   }
   uint32_t key[E];
-  load_keys<E>(smp + (int64_t)r * S, n, true, key);
+  load_keys<E, true>(smp + (int64_t)r * S, n, key);
   uint32_t T, rem;
   radix_select<E>(key, (int)kk, sh, T, rem);
   if (threadIdx.x == 0) thr[r] = T;

@@ -272,13 +272,14 @@ __device__ __forceinline__ void ordered_emit(const uint32_t (&key)[E], uint32_t 
   }
 }
 
-// Thread t's keys t*E .. t*E + E - 1 of a segment of n (invalid slots: 0). vec: the
+// Thread t's keys t*E .. t*E + E - 1 of a segment of n (invalid slots: 0). VEC: the
 // segment is 16-byte aligned and every group of four that starts before n lies in the
-// row, so groups load as one 16-byte access.
-template <int E>
-__device__ __forceinline__ void load_keys(const float* seg, int n, bool vec, uint32_t (&key)[E]) {
+// row, so groups load as one 16-byte access. (A compile-time choice: kernels are built
+// once for each, so the 16-byte form's code does not carry the other.)
+template <int E, bool VEC>
+__device__ __forceinline__ void load_keys(const float* seg, int n, uint32_t (&key)[E]) {
   const int base = threadIdx.x * E;
-  if (vec) {
+  if constexpr (VEC) {
 #pragma unroll
     for (int j = 0; j < E / 4; ++j) {
       const int i = base + 4 * j;
@@ -289,8 +290,14 @@ __device__ __forceinline__ void load_keys(const float* seg, int n, bool vec, uin
       key[4 * j + 3] = i + 3 < n ? order_key(v.w) : 0u;
     }
   } else {
+    // every load issued before any is used (indices clamped into the segment): a load
+    // under the test of its own index would wait for its data before the next starts
+    const int last = n > 0 ? n - 1 : 0;
+    float v[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(seg[base + e]) : 0u;
+    for (int e = 0; e < E; ++e) v[e] = seg[base + e < n ? base + e : last];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(v[e]) : 0u;
   }
 }
 

@@ -62,8 +62,8 @@ __device__ __forceinline__ void load_candidates(const TopkArgs& a, int r, int64_
 // E - 1, keys key_base + position) outside the candidate groups read as -inf; bits
 // start at group g0. With groups of whole quads (key_base and base are multiples of 4)
 // one test covers a 16-byte load.
-template <int E>
-__device__ __forceinline__ void load_keys_masked(const float* seg, int n, bool vec, const TopkArgs& a,
+template <int E, bool VEC>
+__device__ __forceinline__ void load_keys_masked(const float* seg, int n, const TopkArgs& a,
                                                  int64_t key_base, int64_t g0, const uint32_t* bits,
                                                  uint32_t (&key)[E]) {
   const int base = threadIdx.x * E;
@@ -71,7 +71,7 @@ __device__ __forceinline__ void load_keys_masked(const float* seg, int n, bool v
   int grp = (int)(k0 / a.group - g0);
   int rem = (int)(k0 % a.group);
   const uint32_t ninf = order_key(-__builtin_inff());
-  if (vec && a.group % 4 == 0) {
+  if (VEC && a.group % 4 == 0) {
 #pragma unroll
     for (int j = 0; j < E / 4; ++j) {
       const int i = base + 4 * j;
@@ -89,10 +89,15 @@ __device__ __forceinline__ void load_keys_masked(const float* seg, int n, bool v
     }
     return;
   }
+  // every load issued before any is used (clamped indices), as in load_keys
+  const int last = n > 0 ? n - 1 : 0;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = seg[base + e < n ? base + e : last];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool in = (bits[grp >> 5] >> (grp & 31)) & 1u;
-    key[e] = base + e < n ? (in ? order_key(seg[base + e]) : ninf) : 0u;
+    key[e] = base + e < n ? (in ? order_key(v[e]) : ninf) : 0u;
     if (++rem == a.group) {
       rem = 0;
       ++grp;
@@ -115,7 +120,7 @@ constexpr int kWavesPerSimd = E >= 24 ? 8 : 4;
 
 // One workgroup per row. MASK: keys outside the row's candidate groups read as -inf
 // (a consumer's masking folded into the load; the logits are not written).
-template <int E, bool MASK>
+template <int E, bool MASK, bool VEC>
 __device__ __forceinline__ void topk_row_body(const TopkArgs& a, SelShared& sh, CandShared& cs, uint32_t* bits) {
   const int r = blockIdx.x;
   const int n = row_valid(a, r);
@@ -126,31 +131,31 @@ __device__ __forceinline__ void topk_row_body(const TopkArgs& a, SelShared& sh, 
   }
   if constexpr (MASK) load_candidates(a, r, 0, (n + a.group - 1) / a.group, bits);
   uint32_t key[E];
-  if constexpr (MASK) load_keys_masked<E>(a.logits + (int64_t)r * a.ld, n, a.vec, a, 0, 0, bits, key);
-  else load_keys<E>(a.logits + (int64_t)r * a.ld, n, a.vec, key);
+  if constexpr (MASK) load_keys_masked<E, VEC>(a.logits + (int64_t)r * a.ld, n, a, 0, 0, bits, key);
+  else load_keys<E, VEC>(a.logits + (int64_t)r * a.ld, n, key);
   const int base = threadIdx.x * E;
   select_topk<E>(key, a.k, sh, cs, [&](int e) { return base + e; },
                  [&](uint32_t pos, uint32_t, int32_t i) { out[pos] = i; });
 }
 
-template <int E>
+template <int E, bool VEC>
 __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
-  topk_row_body<E, false>(a, sh, cs, nullptr);
+  topk_row_body<E, false, VEC>(a, sh, cs, nullptr);
 }
 
-template <int E>
+template <int E, bool VEC>
 __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_row_masked_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
   __shared__ uint32_t bits[kMaskWords];
-  topk_row_body<E, true>(a, sh, cs, bits);
+  topk_row_body<E, true, VEC>(a, sh, cs, bits);
 }
 
 // Blocked mode, stage 1: top-k candidates (key, index) of one key block of one row, in
 // index order, padded with key 0 to kp. MASK as for the row kernel.
-template <int E, bool MASK>
+template <int E, bool MASK, bool VEC>
 __device__ __forceinline__ void topk_stage1_body(const TopkArgs& a, SelShared& sh, CandShared& cs, uint32_t* bits) {
   const int r = blockIdx.y;
   const int bb = blockIdx.x + a.blk0;
@@ -178,8 +183,8 @@ __device__ __forceinline__ void topk_stage1_body(const TopkArgs& a, SelShared& s
     return;
   }
   uint32_t key[E];
-  if constexpr (MASK) load_keys_masked<E>(row, n, a.vec, a, i0, g0, bits, key);
-  else load_keys<E>(row, n, a.vec, key);
+  if constexpr (MASK) load_keys_masked<E, VEC>(row, n, a, i0, g0, bits, key);
+  else load_keys<E, VEC>(row, n, key);
   const int base = i0 + threadIdx.x * E;
   for (int i = a.k + threadIdx.x; i < a.kp; i += kNT) {   // padding past k
     ck[i] = 0u;
@@ -191,19 +196,19 @@ __device__ __forceinline__ void topk_stage1_body(const TopkArgs& a, SelShared& s
   });
 }
 
-template <int E>
+template <int E, bool VEC>
 __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
-  topk_stage1_body<E, false>(a, sh, cs, nullptr);
+  topk_stage1_body<E, false, VEC>(a, sh, cs, nullptr);
 }
 
-template <int E>
+template <int E, bool VEC>
 __global__ __launch_bounds__(kNT, kWavesPerSimd<E>) void topk_stage1_masked_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ CandShared cs;
   __shared__ uint32_t bits[kMaskWords];
-  topk_stage1_body<E, true>(a, sh, cs, bits);
+  topk_stage1_body<E, true, VEC>(a, sh, cs, bits);
 }
 
 // Blocked mode, stage 2: merge the candidates of all key blocks of one row (they are in
@@ -271,14 +276,18 @@ size_t topk_ws_bytes(int32_t n_rows, int64_t ld, int32_t k) {
 
 template <int E>
 static void launch_row(const TopkArgs& a, hipStream_t st) {
-  if (a.cand) hipLaunchKernelGGL(topk_row_masked_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
-  else hipLaunchKernelGGL(topk_row_kernel<E>, dim3(a.n_rows), dim3(kNT), 0, st, a);
+  if (a.cand && a.vec) hipLaunchKernelGGL((topk_row_masked_kernel<E, true>), dim3(a.n_rows), dim3(kNT), 0, st, a);
+  else if (a.cand) hipLaunchKernelGGL((topk_row_masked_kernel<E, false>), dim3(a.n_rows), dim3(kNT), 0, st, a);
+  else if (a.vec) hipLaunchKernelGGL((topk_row_kernel<E, true>), dim3(a.n_rows), dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL((topk_row_kernel<E, false>), dim3(a.n_rows), dim3(kNT), 0, st, a);
 }
 
 template <int E>
-static void launch_stage1(const TopkArgs& a, hipStream_t st) {
-  if (a.cand) hipLaunchKernelGGL(topk_stage1_masked_kernel<E>, dim3(a.nblk, a.n_rows), dim3(kNT), 0, st, a);
-  else hipLaunchKernelGGL(topk_stage1_kernel<E>, dim3(a.nblk, a.n_rows), dim3(kNT), 0, st, a);
+static void launch_stage1(const TopkArgs& a, hipStream_t st, dim3 grid) {
+  if (a.cand && a.vec) hipLaunchKernelGGL((topk_stage1_masked_kernel<E, true>), grid, dim3(kNT), 0, st, a);
+  else if (a.cand) hipLaunchKernelGGL((topk_stage1_masked_kernel<E, false>), grid, dim3(kNT), 0, st, a);
+  else if (a.vec) hipLaunchKernelGGL((topk_stage1_kernel<E, true>), grid, dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL((topk_stage1_kernel<E, false>), grid, dim3(kNT), 0, st, a);
 }
 
 template <int E>
@@ -336,11 +345,12 @@ tf_status launch_topk(const float* logits, int64_t ld, int32_t n_rows, const int
   a.ws_key = (uint32_t*)ws;
   a.ws_idx = (int32_t*)((char*)ws + (size_t)n_rows * nb * a.kp * 4);
   if (n_rows > 65535) return set_error(TF_E_RANGE, "tf_topk_blocks: at most 65535 rows in blocked mode");
+  const dim3 g1((unsigned)a.nblk, (unsigned)n_rows);
   switch (run_for(B)) {
-    case 4: launch_stage1<4>(a, st); break;
-    case 8: launch_stage1<8>(a, st); break;
-    case 16: launch_stage1<16>(a, st); break;
-    default: launch_stage1<32>(a, st); break;
+    case 4: launch_stage1<4>(a, st, g1); break;
+    case 8: launch_stage1<8>(a, st, g1); break;
+    case 16: launch_stage1<16>(a, st, g1); break;
+    default: launch_stage1<32>(a, st, g1); break;
   }
   tf_status s = launch_status("tf_topk_blocks");
   if (s != TF_OK) return s;
@@ -391,11 +401,12 @@ tf_status launch_topk_block(const float* logits_blk, int32_t B, int32_t b, int32
   TopkArgs a = block_args(logits_blk, B, nb, ncap, n_rows, n_valid, k, nullptr, cand);
   a.blk0 = b;
   a.key0 = (int64_t)b * B;
+  const dim3 g1(1, (unsigned)n_rows);
   switch (run_for(B)) {
-    case 4: hipLaunchKernelGGL(topk_stage1_kernel<4>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(topk_stage1_kernel<8>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
-    case 16: hipLaunchKernelGGL(topk_stage1_kernel<16>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
-    default: hipLaunchKernelGGL(topk_stage1_kernel<32>, dim3(1, n_rows), dim3(kNT), 0, st, a); break;
+    case 4: launch_stage1<4>(a, st, g1); break;
+    case 8: launch_stage1<8>(a, st, g1); break;
+    case 16: launch_stage1<16>(a, st, g1); break;
+    default: launch_stage1<32>(a, st, g1); break;
   }
   return launch_status("tf_indexer_topk");
 }

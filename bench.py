@@ -69,8 +69,8 @@ ENTRIES = {
     "indexer_topk_fused": (("tf::indexer_tile_kernel<16, 128, 2, 2>", "tf::fused_threshold_kernel<32> [grid 131072]",
                             "tf::indexer_tile_kernel<16, 128, 2, 3>", "tf::fused_select_kernel<16, 128> [grid 262144]"),
                            "indexer.hip"),
-    "topk": (("tf::topk_stage1_kernel<4>", "tf::topk_stage2_kernel<4> [grid 8192]"), "topk.hip"),
-    "topk_prefill": (("tf::topk_row_kernel<28>",), "topk.hip"),
+    "topk": (("tf::topk_stage1_kernel<4, true>", "tf::topk_stage2_kernel<4> [grid 8192]"), "topk.hip"),
+    "topk_prefill": (("tf::topk_row_kernel<28, true>",), "topk.hip"),
     "attention": (("tf::attn_decode_kernel", "tf::attn_merge_kernel"), "attention.hip"),
     "attention_prefill": (("tf::attn_kernel_w32",), "attention.hip"),
     "attention_dense": (("tf::attn_dense_kernel_w32",), "attention.hip"),
