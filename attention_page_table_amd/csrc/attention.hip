@@ -1101,14 +1101,18 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     acc.z += f != 0.f ? v[u].z * f : 0.f;
     acc.w += f != 0.f ? v[u].w * f : 0.f;
   }
-  for (int s = kMergeBatch; s < a.nsplit; ++s) {
-    const float f = wgt[s];
-    if (f != 0.f) {
-      const float4 x = *(const float4*)(po + (int64_t)s * 32 * kLatent);
-      acc.x += x.x * f;
-      acc.y += x.y * f;
-      acc.z += x.z * f;
-      acc.w += x.w * f;
+  // more splits (long block lists): the same, a batch of loads in flight at a time
+  for (int s0 = kMergeBatch; s0 < a.nsplit; s0 += kMergeBatch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      v[u] = *(const float4*)(po + (int64_t)(s0 + u < a.nsplit ? s0 + u : a.nsplit - 1) * 32 * kLatent);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float f = s0 + u < a.nsplit ? wgt[s0 + u] : 0.f;
+      acc.x += f != 0.f ? v[u].x * f : 0.f;
+      acc.y += f != 0.f ? v[u].y * f : 0.f;
+      acc.z += f != 0.f ? v[u].z * f : 0.f;
+      acc.w += f != 0.f ? v[u].w * f : 0.f;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -24,7 +24,7 @@ import attention_page_table_amd as tf
 from oracle import workload as ow
 from synth.configs import Workload, tiny
 from synth.device import alloc_pool, populate, query_inputs
-from tests.gpu_common import check_topk_against_oracle, host
+from tests.gpu_common import check_attention, check_topk_against_oracle, host
 
 pytestmark = pytest.mark.gpu
 
@@ -211,3 +211,24 @@ def test_fused_reused_workspace_without_n_valid():
         tf.indexer_topk_fused(plan, P.view(), rs, rp, iq, w, ld, k, got, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_decode_attention_long_block_lists(k):
+    """Decode rows (fewer than 128) with up to 2,048 selected blocks (8,192 tokens): the
+    decode attention kernel runs up to 64 splits a row and the merge combines them in
+    batches; against the oracle on the GPU's own blocks."""
+    _log(f"decode attention: k={k}, 32 heads, merge over up to {k // 32} splits")
+    wl0, plan, P = _pool(128)
+    wl = dataclasses.replace(wl0, Hq=32)
+    rows = [(0, 39999), (1, 35999), (0, 20000), (1, 9000), (0, 4000)]
+    ld = 10000
+    rs, rp, iq, w, q = query_inputs(wl, 0, rows)
+    blocks, nv = _reference(plan, P, rs, rp, iq, w, ld, k)
+    out = torch.empty((len(rows), 32, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((len(rows), 32), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(576.0)
+    tf.sparse_mla_attn(plan, P.view(), rs, rp, q, scale, blocks, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = ow.attention(wl, 0, rows, host(blocks), scale)
+    check_attention(host(out), host(lse), ro, rl, f"k={k}")
