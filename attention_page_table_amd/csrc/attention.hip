@@ -181,6 +181,52 @@ __device__ __forceinline__ int64_t row_base(const AttnArgs& a, int32_t tt) {
   return (int64_t)(tt >> 9) * a.v.page_bytes + a.v.cache_off;
 }
 
+// The token table of a workgroup's slots [j0, j1) (ntiles tiles of kTileTok tokens; slot
+// j0 + q holds block q's four tokens): entry 4 q + c = page * 512 + slot of token
+// 4 blk + c, or kMasked (no block, or past the row's position), or kUnreadable (the
+// table names no page; `bad` is set). A thread takes blocks tid, tid + 256, ..: all
+// their block ids are loaded at once (slots clamped into the list, the clamped ones
+// dropped), then all their page ids (a block's four tokens share a page), so the table
+// costs two dependent loads, not two per 256 tokens.
+template <bool DENSE>
+__device__ __forceinline__ void build_token_table(const AttnArgs& a, int r, int b, int t, int j0, int j1, int ntiles,
+                                                  int32_t* tt, int32_t& bad, int tid) {
+  constexpr int kBPT = kMaxWgTok / kPoolRatio / 256;   // blocks a thread takes at most
+  const int nb = ntiles * kTileTok / kPoolRatio;
+  int blk[kBPT];
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    const int q = tid + 256 * u, slot = j0 + q;
+    const int raw = DENSE ? slot : block_at(a, r, slot < j1 ? slot : (j1 > j0 ? j1 - 1 : 0));
+    blk[u] = q < nb && slot < j1 ? raw : -1;
+  }
+  const bool b_ok = b >= 0 && b < a.v.n_streams;
+  int page[kBPT];
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    const int pi = blk[u] >= 0 ? blk[u] * kPoolRatio / kPageRows : 0;
+    const bool in_tab = blk[u] >= 0 && b_ok && pi < a.v.pt_stride;
+    const int64_t idx = in_tab ? (int64_t)b * a.v.pt_stride + pi : 0;
+    const int p = a.v.pt ? a.v.pt[idx] : (int)idx;
+    page[u] = in_tab && p >= 0 && p < a.v.n_pages ? p : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    const int q = tid + 256 * u;
+    if (q >= nb) continue;
+#pragma unroll
+    for (int c = 0; c < kPoolRatio; ++c) {
+      const int s = blk[u] * kPoolRatio + c;
+      int32_t e = kMasked;
+      if (blk[u] >= 0 && s <= t) {
+        e = page[u] >= 0 ? page[u] * kPageRows + (s % kPageRows) : kUnreadable;
+        if (page[u] < 0) bad = 1;
+      }
+      tt[kPoolRatio * q + c] = e;
+    }
+  }
+}
+
 // Pieces of one tile a thread loads: bf16 rows are 64 latent + 8 rope 16-byte
 // pieces per token (9 per thread); fp8 rows 32 + 8 (5 per thread).
 template <bool FP8>
@@ -428,18 +474,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   if (tid == 0) sh.bad = 0;
   __syncthreads();
   // ---- token table ----------------------------------------------------------------
-  for (int i = tid; i < ntiles * kTileTok; i += 256) {
-    const int slot = j0 + i / kPoolRatio;
-    const int blk = slot < j1 ? block_at(a, r, slot) : -1;
-    const int s = blk * kPoolRatio + (i & 3);
-    int32_t e = kMasked;
-    if (blk >= 0 && s <= t) {
-      const int page = page_of(a.v, b, s / kPageRows);
-      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
-      if (page < 0) sh.bad = 1;
-    }
-    sh.tt[i] = e;
-  }
+  build_token_table<false>(a, r, b, t, j0, j1, ntiles, sh.tt, sh.bad, tid);
   // ---- query fragments --------------------------------------------------------------
   bf16x8 aq[F::kSteps];
   {
@@ -638,18 +673,7 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
   }
   __syncthreads();
   // ---- token table ----------------------------------------------------------------
-  for (int i = tid; i < ntiles * kTileTok; i += 256) {
-    const int slot = j0 + i / kPoolRatio;
-    const int blk = slot < j1 ? (DENSE ? slot : block_at(a, r, slot)) : -1;
-    const int s = blk * kPoolRatio + (i & 3);
-    int32_t e = kMasked;
-    if (blk >= 0 && s <= t) {
-      const int page = page_of(a.v, b, s / kPageRows);
-      e = page >= 0 ? page * kPageRows + (s % kPageRows) : kUnreadable;
-      if (page < 0) sh.bad = 1;
-    }
-    sh.tt[i] = e;
-  }
+  build_token_table<DENSE>(a, r, b, t, j0, j1, ntiles, sh.tt, sh.bad, tid);
   // ---- query fragments (A: head = lane % 32, this wave's dims) ------------------------
   bf16x8 aq[F::kSteps];
   {
