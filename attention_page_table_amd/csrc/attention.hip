@@ -91,12 +91,14 @@ __device__ __forceinline__ int split_end(const AttnArgs& a, int j0, int t) {
   return a.blocks ? (j0 + a.slots_per_split < a.k ? j0 + a.slots_per_split : a.k) : dense_split_end(a, j0, t);
 }
 
-// Row stride of the partial S tiles in floats: 16-byte aligned rows (vector reads in
-// the softmax), and the rows one MFMA store instruction writes land on disjoint LDS
-// banks (32x32 tiles: the two half-waves' rows are 4 apart, 4 x 40 = 32 banks mod 64;
-// 16x16 tiles: the four lane groups' rows are 4 apart, 4 x 36 = 16 banks mod 64).
+// Row stride of the partial S tiles in floats, 16-byte aligned rows (vector reads in
+// the softmax). 32x32 tiles: unpadded. Their 4-byte stores (one MFMA result: two rows
+// of 32 tokens) measured free of bank conflicts at every stride tried, and the
+// softmax's 16-byte reads (eight lanes a head, consecutive heads) are conflict-free
+// only when a row is 128 bytes long: at 36 or 40 floats they cost 4 and 8 conflict
+// cycles per read. 16x16 tiles: 36 (the four lane groups' rows 4 apart).
 template <int HG>
-constexpr int kSpartStride = HG == 32 ? kTileTok + 8 : kTileTok + 4;
+constexpr int kSpartStride = HG == 32 ? kTileTok : kTileTok + 4;
 
 template <int HG>
 struct alignas(16) AttnShared {
@@ -556,14 +558,41 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 // and issues the next tile's gather into the same registers. No wave reads another's
 // keys, so a tile needs two barriers (partial S -> softmax, softmax -> P.V) besides the
 // one inside the softmax, and LDS carries each value twice instead of three times.
-constexpr int kVS = 144;   // row stride of a wave's V slice, bf16: 288 bytes, conflict-free
-                           // for the transposed reads (rows 32 banks apart)
+// LDS layouts of the sliced kernels, chosen by measured bank conflicts per instruction
+// (no padded stride served both access forms of a tile):
+// * a wave's V slice, 32 tokens x 128 columns: rows of 160 bf16 (the P.V transposed
+//   reads, four rows x 64 bytes per half-wave, then land on disjoint banks), and the
+//   16-byte piece c of row t stored at piece c ^ ((t >> 1) & 3), which spreads the
+//   slice's 16-byte stores (consecutive tokens, one piece) over the banks. Unswizzled,
+//   the stores cost 24 conflict cycles each at this stride; at 144 (stores 8, reads 2)
+//   and 152 (0 and 2) no stride reached zero for both;
+// * P (32 heads x 32 tokens): unpadded 64-byte rows, piece c of head h at
+//   c ^ ((h >> 2) & 3): the softmax's 8-byte stores (four heads a half-wave) and P.V's
+//   16-byte reads (16 heads, one piece) are both conflict-free, where 80-byte rows cost
+//   the stores 4 cycles each.
+constexpr int kVS = 160;
+__device__ __forceinline__ int vslice_at(int t, int c) {   // bf16 offset of column c of token t
+  return t * kVS + (((c >> 3) ^ ((t >> 1) & 3)) << 3) + (c & 7);
+}
+constexpr int kPS = kTileTok;
+__device__ __forceinline__ int p_at(int h, int c) {        // bf16 offset of token c of head h
+  return h * kPS + (((c >> 3) ^ ((h >> 2) & 3)) << 3) + (c & 7);
+}
+// bfrag_tr over the swizzled V slice: rows k0 + j / 4 and k0 + 4 + j / 4, columns
+// n0 + 4 (j % 4) .. + 3 (n0 a multiple of 8: a lane's 8 bytes stay in one piece).
+__device__ __forceinline__ bf16x8 bfrag_tr_vslice(const __bf16* tile, int k0, int n0, int j) {
+  const int r = k0 + (j >> 2), c = n0 + 4 * (j & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + vslice_at(r, c)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + vslice_at(r + 4, c)));
+  const short __attribute__((ext_vector_type(8))) v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 struct alignas(16) AttnSharedW {
-  __bf16 vt[4][kTileTok][kVS];   // wave w: tokens x its 128 latent columns
+  __bf16 vt[4][kTileTok * kVS];   // wave w: tokens x its 128 latent columns (vslice_at)
   float spart[4][32][kSpartStride<32>];
-  __bf16 p_hi[32][kTileTok + 8];
-  __bf16 p_lo[32][kTileTok + 8];
+  __bf16 p_hi[32 * kPS];          // p_at
+  __bf16 p_lo[32 * kPS];
   float tsc[kTileTok];
   int32_t tt[kMaxWgTok];
   float m_run[32], l_run[32], alpha[32];
@@ -617,8 +646,8 @@ __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t
     phv[e] = hi;
     plv[e] = bf16_rne(pv - bf16_to_f(hi));
   }
-  *(bv_t*)&sh.p_hi[h][p * TPT] = phv;
-  *(bv_t*)&sh.p_lo[h][p * TPT] = plv;
+  *(bv_t*)&sh.p_hi[p_at(h, p * TPT)] = phv;
+  *(bv_t*)&sh.p_lo[p_at(h, p * TPT)] = plv;
   lsum = group_sum<TPH>(lsum);
   // the other parity's flag was last read in the previous tile's P.V (done: a barrier
   // since), and is next set in the next tile's softmax (a barrier after this one)
@@ -742,7 +771,7 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
     }
   };
   if (ntiles > 0) gather(0);
-  __bf16* vt = &sh.vt[wave][0][0];
+  __bf16* vt = &sh.vt[wave][0];
   for (int it = 0; it < ntiles; ++it) {
     // ---- S partial from the registers ------------------------------------------------
     if constexpr (FP8) widen();
@@ -753,7 +782,7 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
     accr = F::mfma(aq[8], kvr[8], accr);
     // ---- the slice's latent columns to this wave's LDS region, then the next gather ----
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(bf16x8*)&vt[tok * kVS + (FP8 ? 64 * g + 8 * i : 16 * i + 8 * g)] = kvr[i];
+    for (int i = 0; i < 8; ++i) *(bf16x8*)&vt[vslice_at(tok, FP8 ? 64 * g + 8 * i : 16 * i + 8 * g)] = kvr[i];
     if (it + 1 < ntiles) gather(it + 1);
 #pragma unroll
     for (int i = 0; i < F::kAccN; ++i)
@@ -777,13 +806,13 @@ __device__ __forceinline__ void attn_w32_body(const AttnArgs& a, AttnSharedW& sh
 #pragma unroll
       for (int ks = 0; ks < F::kPVsteps; ++ks) {
         const int tk = ks * F::kPVk + ahalf * 8;
-        const bf16x8 ph = *(const bf16x8*)&sh.p_hi[arow][tk];
-        const bf16x8 pl = *(const bf16x8*)&sh.p_lo[arow][tk];
+        const bf16x8 ph = *(const bf16x8*)&sh.p_hi[p_at(arow, tk)];
+        const bf16x8 pl = *(const bf16x8*)&sh.p_lo[p_at(arow, tk)];
 #pragma unroll
         for (int nt = 0; nt < F::kNT; ++nt) {
           const int k0 = ks * F::kPVk + (grp >> 1) * 8;
           const int n0 = nt * F::kNTW + (grp & 1) * 16;
-          const bf16x8 vb = bfrag_tr(vt, kVS, k0, n0, j);
+          const bf16x8 vb = bfrag_tr_vslice(vt, k0, n0, j);
           o[nt] = F::mfma(ph, vb, o[nt]);
           o[nt] = F::mfma(pl, vb, o[nt]);
         }
