@@ -375,19 +375,28 @@ def bench_decode(tf, args):
     ms_per_step = t_start.elapsed_time(t_end) / K
 
     # ------------------------------------------------------------------ per-call durations
-    # `call_steps` further steps, an event between every call: each call's mean over its
-    # launches (launch to launch, so each also holds one dispatch gap)
+    # Whole steps again, `call_steps` of them for each of five placements of a second event:
+    # right after the step's start event (nothing between: what an event itself adds), or
+    # after call c. Every step runs all four calls; each interval holds one event's own
+    # dispatch, so call c's duration in the step is the difference of the mean intervals
+    # ending after c and after the call before it, and the event's cost cancels.
     S = max(50, args.call_steps)
-    ev = [[TimingEvent() for _ in range(5)] for _ in range(S)]
-    for i in range(S):
-        ls = launches[i % len(launches)]
-        ev[i][0].record()
-        for c in range(4):
-            ls[c]()
-            ev[i][c + 1].record()
-    torch.cuda.synchronize()
-    per = {n: [ev[i][c].elapsed_time(ev[i][c + 1]) * 1e3 for i in range(S)] for c, n in enumerate(names)}
-    avg_us = {n: _mean(v) for n, v in per.items()}
+    cum = []
+    for c in range(-1, 4):
+        e0, e1 = [TimingEvent() for _ in range(S)], [TimingEvent() for _ in range(S)]
+        for i in range(S):
+            ls = launches[i % len(launches)]
+            e0[i].record()
+            if c < 0:
+                e1[i].record()
+            for j in range(4):
+                ls[j]()
+                if j == c:
+                    e1[i].record()
+        torch.cuda.synchronize()
+        cum.append([e0[i].elapsed_time(e1[i]) * 1e3 for i in range(S)])
+    avg_us = {n: _mean(cum[c + 1]) - _mean(cum[c]) for c, n in enumerate(names)}
+    med_us = {n: _median(cum[c + 1]) - _median(cum[c]) for c, n in enumerate(names)}
     dom = max(["indexer", "topk", "attention"], key=lambda n: avg_us[n])
 
     lat_bytes = R * wl.k * 4 * ROW_BYTES                       # selected latent + rope rows
@@ -399,7 +408,7 @@ def bench_decode(tf, args):
         "attention": lat_bytes + R * wl.Hq * 576 * 2 + R * wl.Hq * (512 + 1) * 4 + R * wl.k * 4 + R * 8,
     }
     value = (lat_bytes + key_bytes) / (ms_per_step * 1e-3) / 1e9
-    kern = {n: {"us": round(avg_us[n], 3), "us_median": round(_median(per[n]), 3), "alg_bytes": alg_bytes[n],
+    kern = {n: {"us": round(avg_us[n], 3), "us_median": round(med_us[n], 3), "alg_bytes": alg_bytes[n],
                 "GBps": round(alg_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1)} for n in names}
     achieved = alg_bytes[dom] / (avg_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -447,7 +456,8 @@ def bench_decode(tf, args):
                            "value": "paged-cache bytes one decode step reads (visible pooled keys + selected "
                                     "latent and rope rows) / time per step",
                            "launches": "eager, marshalled once",
-                           "kernels_timing": f"mean of {S} launches per call, an event between every call"},
+                           "kernels_timing": f"per call: differences of mean event intervals from a step's start to "
+                                  f"after the call and after the call before it, {S} steps each"},
                 "decode_attention_latent": headline,
                 "decode_indexer_keys": indexer_scan,
                 "decode_fused_indexer_topk": fused_res,
@@ -1230,8 +1240,9 @@ def summarize_trace(db, label, command, bench_json=None):
             f"{n} ({a:.2f})" for n, _, a in ks))
     if bench_json:
         b = json.loads([ln for ln in open(bench_json) if ln.startswith("{")][-1])
-        lines += ["", "# HIP events in an unprofiled run of the same command (launch to launch, so each also holds"
-                      " one dispatch gap) vs the kernels' own durations above"]
+        lines += ["", "# HIP events in an unprofiled run of the same command vs the kernels' own durations above"
+                      " (decode calls: differences of intervals from the step's start, so no event's own dispatch"
+                      " is counted; the prefill and dense calls: event to event, one dispatch included)"]
         ev = {n: d["us"] for n, d in b["kernels"].items()}
         if b.get("prefill_indexer"):
             ev["indexer_prefill"] = b["prefill_indexer"]["us"]
