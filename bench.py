@@ -422,7 +422,7 @@ def bench_decode(tf, args):
                 "latent_GBps": round(att_gbs, 1), "frac_hbm": round(att_gbs / HBM_PEAK_GBS, 4),
                 "timed_launches": S,
                 "note": "selected latent + rope rows gathered (8 rows x 2,048 tokens x 1,152 B) / the call's "
-                        "mean event interval"}
+                        "duration in the step"}
     indexer_scan = {"call": "tf_indexer_logits", "key_bytes": key_bytes, "us": round(avg_us["indexer"], 2),
                     "key_GBps": round(key_bytes / (avg_us["indexer"] * 1e-6) / 1e9, 1)}
     # the fused indexer + top-k on the same rows (no logits written), against the pair
