@@ -125,11 +125,15 @@ __device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
   return (uint16_t)(sign | ((e - 7u + 127u) << 7) | (m << 4));
 }
 
-__device__ __forceinline__ __bf16 bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  return __builtin_bit_cast(__bf16, (uint16_t)u);
-}
+// Nearest bf16, ties to even: the conversion instruction (v_cvt_pk_bf16_f32), where
+// integer rounding took four instructions a value (the same bits for finite values, the
+// only ones converted here: softmax weights and their residues).
+__device__ __forceinline__ __bf16 bf16_rne(float x) { return (__bf16)x; }
+
+// 2^x for a softmax weight (x <= 8): v_exp_f32 alone. exp2f adds a rescaling for
+// x < -126 only, where the weight is below 2^-126 of the largest in its row and
+// contributes nothing an fp32 sum keeps.
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bf16_to_f(__bf16 x) {
   return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, x)) << 16);
@@ -383,7 +387,7 @@ __device__ __forceinline__ void softmax_tile(SH& sh, const int32_t* tt, const fl
 #pragma unroll
   for (int e = 0; e < TPT; ++e) {
     const int tok = p * TPT + e;
-    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
+    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2_weight(z[e] - m_new);
     lsum += pe;
     const float pv = FP8 ? pe * tsc[tok] : pe;
     const __bf16 hi = bf16_rne(pv);
@@ -639,7 +643,7 @@ __device__ __forceinline__ void softmax_tile_lazy(AttnSharedW& sh, const int32_t
   bv_t phv, plv;
 #pragma unroll
   for (int e = 0; e < TPT; ++e) {
-    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2f(z[e] - m_new);
+    const float pe = z[e] == -__builtin_inff() ? 0.f : exp2_weight(z[e] - m_new);
     lsum += pe;
     const float pv = FP8 ? pe * sh.tsc[p * TPT + e] : pe;   // fp8 rows: the row scale joins P
     const __bf16 hi = bf16_rne(pv);
@@ -1005,7 +1009,7 @@ __global__ __launch_bounds__(512, 1) void attn_decode_kernel(AttnArgs a) {
       float m = wm[0][i];
 #pragma unroll
       for (int w = 1; w < kDecWaves; ++w) m = __builtin_fmaxf(m, wm[w][i]);
-      const float p = z[i] == -__builtin_inff() ? 0.f : exp2f(z[i] - m);
+      const float p = z[i] == -__builtin_inff() ? 0.f : exp2_weight(z[i] - m);
       const float ps = group_sum<16>(p);
       if ((lane & 15) == 0) sh.wsum[wave][h] = ps;
       if (wave == 0 && (lane & 15) == 0) sh.m_run[h] = m;
