@@ -197,10 +197,120 @@ __device__ void index_one_row(const IdxArgs& a, int row, int64_t kb, int64_t ke,
   for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) out[key] = ninf;
 }
 
+// Four rows whose streams name the same pages over most of [kb, ke) (a prefix held by
+// reference, [#1732] "What this changes"): each shared page is loaded once for all
+// four rows. Wave w scores subtiles w, w + 4, w + 8, ... of the range (the w-th 32 keys
+// of each page) for the four rows, as two MFMA tiles of two rows x 16 heads (lanes
+// 0..31 hold the first row of a tile, lanes 32..63 the second; a lane holds one key and
+// all 16 heads). A page the four do not share (bit i of shared clear for page
+// kb / 128 + i; pgs[r][i] is row r's page id) is loaded and scored once per row. Each
+// (row, key) is the same MFMA dot product, head sum and store as on the per-row path,
+// so the logits are bit for bit the same.
+template <int D>
+__device__ void index_four_rows_shared(const IdxArgs& a, int row0, int64_t kb, int64_t ke, int wave, int lane,
+                                       const int32_t (*pgs)[64], uint64_t shared) {
+  constexpr int H = 16, KS = D / 16;
+  const int g = lane >> 5, n = lane & 31;
+  const float ninf = -__builtin_inff();
+  const float qnan = __builtin_nanf("");
+  int nc[2] = {0, 0}, ncmax = 0;   // nc[t]: this lane's row of tile t, row0 + 2 t + g
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = nc_of(a, row0 + r);
+    ncmax = c > ncmax ? c : ncmax;
+    if ((r & 1) == g) nc[r >> 1] = c;
+  }
+  const int64_t kend = ke < ncmax ? ke : ncmax;
+  // A fragments as in the tile kernel: A-row m = 8a + 4b + c is head 4a + c of row b
+  bf16x8 af[2][KS];
+  {
+    const int mb = (n >> 2) & 1, head = 4 * (n >> 3) + (n & 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        af[t][ks] = *(const bf16x8*)(a.q + ((int64_t)(row0 + 2 * t + mb) * H + head) * D + ks * 16 + g * 8);
+  }
+  float wv[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wv[t][i] = a.w[(int64_t)(row0 + 2 * t + g) * H + i];
+  float* out0 = a.logits + (int64_t)(row0 + g) * a.ldo;
+  float* out1 = a.logits + (int64_t)(row0 + 2 + g) * a.ldo;
+  const int p0 = (int)(kb / kKeysPerPage);
+  // the page of subtile kt for row r (uniform: read from LDS)
+  auto page_at = [&](int64_t kt, int r) { return pgs[r][(int)(kt / kKeysPerPage) - p0]; };
+  auto load_pg = [&](int pg, int64_t kt, bf16x8 (&bf)[KS]) {
+    if (pg >= 0) {
+      const char* kp = cache_block(a.v, pg) + a.off_pkey + (int64_t)((kt % kKeysPerPage) + n) * a.pkey_row_bytes + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = *(const bf16x8*)(kp + ks * 32);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[ks] = bf16x8{};
+    }
+  };
+  auto load = [&](int64_t kt, bf16x8 (&bf)[KS]) { load_pg(page_at(kt, 0), kt, bf); };
+  // two of the wave's subtiles in flight: slot s holds subtile kb + 32 wave + 128 (2 i + s)
+  // (the row groups of a range request each page at about the same time, so the second
+  // request of a page meets the first in L2)
+  auto step = [&](int64_t kt, bf16x8 (&cur)[KS]) {
+    const int64_t key = kt + n;
+    if (!((shared >> ((int)(kt / kKeysPerPage) - p0)) & 1)) {
+      // a page the rows do not share: each row's own page, scored by the tile that
+      // holds the row; the row's half-wave stores
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pr = page_at(kt, r);
+        load_pg(pr, kt, cur);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r >> 1][ks], cur[ks], acc, 0, 0, 0);
+        const float s = weighted_relu_sum<H>(wv[r >> 1], acc, 0);
+        if (g == (r & 1) && key < ke) {
+          float* o = r >> 1 ? out1 : out0;
+          o[key] = key < nc[r >> 1] ? (pr >= 0 ? s : qnan) : ninf;
+        }
+      }
+      if (kt + 2 * kKeysPerPage < kend) load(kt + 2 * kKeysPerPage, cur);
+      return;
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][ks], cur[ks], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][ks], cur[ks], acc1, 0, 0, 0);
+    }
+    const int pg = page_at(kt, 0);
+    if (kt + 2 * kKeysPerPage < kend) load(kt + 2 * kKeysPerPage, cur);
+    const float s0 = weighted_relu_sum<H>(wv[0], acc0, 0);
+    const float s1 = weighted_relu_sum<H>(wv[1], acc1, 0);
+    if (key < ke) {
+      out0[key] = key < nc[0] ? (pg >= 0 ? s0 : qnan) : ninf;
+      out1[key] = key < nc[1] ? (pg >= 0 ? s1 : qnan) : ninf;
+    }
+  };
+  bf16x8 s0[KS], s1[KS];
+  const int64_t k0 = kb + 32 * wave;
+  if (k0 < kend) load(k0, s0);
+  if (k0 + kKeysPerPage < kend) load(k0 + kKeysPerPage, s1);
+  for (int64_t kt = k0; kt < kend; kt += 2 * kKeysPerPage) {
+    step(kt, s0);
+    if (kt + kKeysPerPage < kend) step(kt + kKeysPerPage, s1);
+  }
+  // keys past every row's compressed length: wave w fills row row0 + w
+  float* o = a.logits + (int64_t)(row0 + wave) * a.ldo;
+  for (int64_t key = (kend > kb ? kend : kb) + lane; key < ke; key += 64) o[key] = ninf;
+}
+
 // Per-row kernel: wave w of workgroup (key group kg, row group rg) takes row 4 rg + w.
 // The row groups of one key group run on one XCD (workgroups 8 apart).
-template <int H, int D, int KIND>
-__global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
+// SHARED (16 heads, whole calls, ranges of several pages, at least four rows): a row
+// group whose streams name the same pages over at least half its range takes the
+// shared-page path (indexer_shared_rows_kernel; the other calls run a kernel without it).
+template <int H, int D, int KIND, bool SHARED>
+__device__ __forceinline__ void rows_body(const IdxArgs& a) {
   constexpr bool SAMPLED = KIND == kSample;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_rg = (a.n_rows + 3) / 4;
@@ -224,7 +334,35 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
     }
   }
   if (kg == 0 && a.n_valid && lane == 0) a.n_valid[row] = nc_of<SAMPLED>(a, row);
+  if constexpr (SHARED && H == 16 && KIND == kWhole) {
+    // where the four streams of a row group name the same pages (a shared prefix) over
+    // at least half the range, load those pages once for the four rows
+    if (ke - kb > kKeysPerPage && (rg + 1) * 4 <= a.n_rows) {
+      __shared__ int32_t pgs[4][64];
+      const int p0 = (int)(kb / kKeysPerPage);
+      const int np = (int)((ke - 1) / kKeysPerPage) - p0 + 1;
+      pgs[wave][lane] = page_of(a.v, a.row_stream[row], p0 + lane);
+      __syncthreads();
+      const bool same =
+          lane < np && pgs[0][lane] == pgs[1][lane] && pgs[0][lane] == pgs[2][lane] && pgs[0][lane] == pgs[3][lane];
+      const uint64_t shared = __ballot(same);
+      if (2 * __builtin_popcountll(shared) >= np) {
+        index_four_rows_shared<D>(a, rg * 4, kb, ke, wave, lane, pgs, shared);
+        return;
+      }
+    }
+  }
   index_one_row<H, D, KIND>(a, row, kb, ke, lane, kg, spec, spec_all);
+}
+
+template <int H, int D, int KIND>
+__global__ __launch_bounds__(256) void indexer_rows_kernel(IdxArgs a) {
+  rows_body<H, D, KIND, false>(a);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void indexer_shared_rows_kernel(IdxArgs a) {
+  rows_body<16, D, kWhole, true>(a);
 }
 
 // ---- tile path -----------------------------------------------------------------------------
@@ -577,7 +715,12 @@ static tf_status launch_hd(IdxArgs a, int32_t n_rows, hipStream_t st, int kind, 
     switch (kind) {
       case kSample: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kSample>), grid, dim3(256), 0, st, a); break;
       case kFilter: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kFilter>), grid, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((indexer_rows_kernel<H, D, kWhole>), grid, dim3(256), 0, st, a); break;
+      default:
+        if (H == 16 && sh.kpw > kKeysPerPage && n_rows >= 4)
+          hipLaunchKernelGGL((indexer_shared_rows_kernel<D>), grid, dim3(256), 0, st, a);
+        else
+          hipLaunchKernelGGL((indexer_rows_kernel<H, D, kWhole>), grid, dim3(256), 0, st, a);
+        break;
     }
   }
   return TF_OK;

@@ -255,11 +255,13 @@ __global__ __launch_bounds__(kNT) void topk_stage2_kernel(TopkArgs a) {
 // and a second launch merges their candidates.
 static int pick_block(int32_t n_rows, int64_t ld, int32_t k) {
   if (ld <= 4096 || (ld <= 32768 && n_rows >= 128)) return 0;
-  // few long rows: blocks of 4,096 .. 32,768 keys so that about 64 workgroups run,
-  // with the merged candidates (blocks x kp) at most 32,768
+  // few long rows: the shortest block of 4,096 .. 32,768 keys with at most 256 stage-1
+  // workgroups (a decode batch of 8 rows x 32,768 keys: 64 blocks of 4,096; 8 rows x
+  // 262,144: 136 of 16,384, which ran 29 against 41 us for 72 of 32,768), with the
+  // merged candidates (blocks x kp) at most 32,768
   const int64_t kp = (k + 3) / 4 * 4;
   int64_t B = 4096;
-  while (B < 32768 && n_rows * ((ld + B - 1) / B) > 64) B *= 2;
+  while (B < 32768 && n_rows * ((ld + B - 1) / B) > 256) B *= 2;
   while (B < 32768 && ((ld + B - 1) / B) * kp > 32768) B *= 2;
   if (((ld + B - 1) / B) * kp > 32768) return -1;
   return (int)B;

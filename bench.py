@@ -63,6 +63,8 @@ CAL_BYTES = 1 << 30            # the calibration stream: read 1 GiB, write 1 GiB
 ENTRIES = {
     "write": (("tf::latent_write_kernel [grid 768]",), "write.hip"),
     "indexer": (("tf::indexer_rows_kernel<16, 128, 0>",), "indexer.hip"),
+    # the shared-prefix decode: row groups whose streams share pages score them once
+    "indexer_shared": (("tf::indexer_shared_rows_kernel<128>",), "indexer.hip"),
     "indexer_prefill": (("tf::indexer_tile_kernel<16, 128, 2, 0>",), "indexer.hip"),
     # the prefill chunk's launches (its threshold and selection kernels by grid: the decode
     # batch's comparison launches the same instances at other sizes)
@@ -807,7 +809,8 @@ def bench_shared_prefix(tf, reps=5):
     populate(P)
     rows = wl.rows
     R = len(rows)
-    ld = max(t // 4 + 1 for _, t in rows)
+    # logits rows padded to 16 bytes, so that top-k loads them 16 bytes at a time
+    ld = (max(t // 4 + 1 for _, t in rows) + 3) // 4 * 4
     scale = 1.0 / math.sqrt(576.0)
     logits = torch.empty((R, ld), dtype=torch.float32, device="cuda")
     nv = torch.empty(R, dtype=torch.int32, device="cuda")
@@ -872,7 +875,7 @@ def bench_shared_prefix(tf, reps=5):
                        "keys_scanned_bytes_per_cache": scanned, "unique_key_bytes_per_cache": unique,
                        "scanned_GBps_mean": round(scanned / (_mean(idx) * 1e-6) / 1e9, 1),
                        "unique_GBps_mean": round(unique / (_mean(idx) * 1e-6) / 1e9, 1),
-                       "traffic": load_traffic("indexer", C4_TRAFFIC_FILE)}}
+                       "traffic": load_traffic("indexer_shared", C4_TRAFFIC_FILE)}}
     del per_cache, keep, P
     torch.cuda.empty_cache()
     return res

@@ -14,8 +14,8 @@ import attention_page_table_amd as tf
 from oracle import Geom, PoolImage
 from oracle import workload as ow
 from oracle.layout import snapshot_copy
-from synth import TAG_LATENT, TAG_PKEY
-from synth.configs import LAT, ROPE, ROW, tiny
+from synth import TAG_LATENT, TAG_PKEY, bf16_to_f64
+from synth.configs import LAT, ROPE, ROW, shared_prefix_decode, tiny
 from synth.device import NAN16, _rid, alloc_pool, fill_bf16, populate, query_inputs
 from tests.gpu_common import check_attention, check_logits, host, logits_bound
 
@@ -73,6 +73,40 @@ def test_indexer_every_instance(H, Dk, path):
     check_logits(host(logits), ref, logits_bound(wl, 0, rows, ld), f"H={H} Dk={Dk} {path}")
     assert np.array_equal(host(nv), ow.n_valid(rows, ld))
 
+
+
+def test_indexer_shared_prefix_rows():
+    """Rows of streams that hold the same prefix pages ([#1732] "What this changes"):
+    a row group of four such streams scores each page once for all four rows (ranges
+    of several pages; the second group takes the pages from the middle of its range
+    first), the last group one row at a time; every logit is the oracle's. Rows 1, 3
+    and 6 stop inside the prefix, so the shared path masks per row; the last key range
+    holds the last shared page and the streams' private tail pages, which the four
+    rows score one at a time."""
+    wl = shared_prefix_decode(0, n_streams=9, n_caches=1, shared_pages=601)
+    _log(f"indexer: shared prefix, {wl.n_pages} pages")
+    plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
+    P = alloc_pool(wl, plan)
+    populate(P)
+    L = wl.lengths
+    rows = [(0, L[0] - 1), (1, 200000), (2, L[2] - 1), (3, 77777), (4, L[4] - 1), (5, L[5] - 1), (6, 250000),
+            (7, L[7] - 1), (8, L[8] - 1)]
+    rs, rp, iq, w, _ = query_inputs(wl, 0, rows)
+    ld = max(t // 4 + 1 for _, t in rows)
+    logits = torch.empty((len(rows), ld), dtype=torch.float32, device="cuda")
+    nv = torch.empty(len(rows), dtype=torch.int32, device="cuda")
+    tf.indexer_logits(plan, P.view(), rs, rp, iq, w, logits, n_valid=nv)
+    torch.cuda.synchronize()
+    ns = wl.shared_tokens // 4
+    shared = ow.keys_of(wl, 0, 0, ns)
+    keys = []
+    for b, t in rows:
+        n = t // 4 + 1
+        keys.append(shared[:n] if n <= ns else
+                    np.concatenate([shared, bf16_to_f64(wl.pkey_bits(0, b, np.arange(ns, n)))]))
+    ref = ow.logits(wl, 0, rows, ld, keys=keys)
+    check_logits(host(logits), ref, logits_bound(wl, 0, rows, ld, keys=keys), "shared prefix")
+    assert np.array_equal(host(nv), ow.n_valid(rows, ld))
 
 def _oracle_image_all_caches(wl, fp8):
     """The oracle's byte image of a pool holding every stream's rows and keys in every cache."""
