@@ -19,8 +19,10 @@
 //    B fragment read from LDS feeds MT tiles. Workgroups whose rows are not all of
 //    one stream take the per-row path.
 //  * row kernel (few rows of distinct streams, e.g. a decode batch; HBM-bound): each
-//    wave streams one row's keys straight into B fragments, one subtile ahead, with
-//    the row's page ids preloaded across the lanes.
+//    wave streams one row's keys straight into B fragments, three subtiles ahead, with
+//    the row's page ids preloaded across the lanes. Its shared-page instance (ranges
+//    of several pages, 16 heads) scores a row group of four streams that name the same
+//    pages (a prefix held by reference) from one load of each page.
 #include <type_traits>
 
 #include "select.h"
