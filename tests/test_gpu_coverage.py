@@ -75,22 +75,23 @@ def test_indexer_every_instance(H, Dk, path):
 
 
 
-def test_indexer_shared_prefix_rows():
+@pytest.mark.parametrize("n_rows", [8, 9])
+def test_indexer_shared_prefix_rows(n_rows):
     """Rows of streams that hold the same prefix pages ([#1732] "What this changes"):
     a row group of four such streams scores each page once for all four rows (ranges
-    of several pages; the second group takes the pages from the middle of its range
-    first), the last group one row at a time; every logit is the oracle's. Rows 1, 3
-    and 6 stop inside the prefix, so the shared path masks per row; the last key range
+    of several pages); every logit is the oracle's. Eight rows make two such groups;
+    nine add a group of one row, scored one row at a time. Rows 1, 3 and 6 stop
+    inside the prefix, so the shared path masks per row; the last key range
     holds the last shared page and the streams' private tail pages, which the four
     rows score one at a time."""
     wl = shared_prefix_decode(0, n_streams=9, n_caches=1, shared_pages=601)
-    _log(f"indexer: shared prefix, {wl.n_pages} pages")
+    _log(f"indexer: shared prefix, {wl.n_pages} pages, {n_rows} rows")
     plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
     P = alloc_pool(wl, plan)
     populate(P)
     L = wl.lengths
     rows = [(0, L[0] - 1), (1, 200000), (2, L[2] - 1), (3, 77777), (4, L[4] - 1), (5, L[5] - 1), (6, 250000),
-            (7, L[7] - 1), (8, L[8] - 1)]
+            (7, L[7] - 1), (8, L[8] - 1)][:n_rows]
     rs, rp, iq, w, _ = query_inputs(wl, 0, rows)
     ld = max(t // 4 + 1 for _, t in rows)
     logits = torch.empty((len(rows), ld), dtype=torch.float32, device="cuda")
