@@ -200,6 +200,9 @@ tf_status tf_latent_write_quantize(const tf_plan* p, tf_kv_view dst, int32_t n_r
  * [n_rows][n_heads], logits fp32 [n_rows][ld]. Products are exact bf16 x bf16,
  * accumulated in fp32 (MFMA); the ReLU, weights and head sum in fp32.
  * n_valid (optional, device int32 [n_rows]) receives n_c.
+ * Rows of streams whose tables name the same pages (a prefix held by reference,
+ * [#1732] "What this changes") may be scored from one read of each shared page;
+ * the results are the same bit for bit.
  * n_heads must be 4, 8 or 16; index_dim 64 or 128; ld >= 1. */
 tf_status tf_indexer_logits(const tf_plan* p, tf_kv_view keys, int32_t n_rows,
                             const int32_t* row_stream, const int32_t* row_pos,
