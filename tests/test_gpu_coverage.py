@@ -75,17 +75,17 @@ def test_indexer_every_instance(H, Dk, path):
 
 
 
-@pytest.mark.parametrize("n_rows", [8, 9])
-def test_indexer_shared_prefix_rows(n_rows):
+@pytest.mark.parametrize("n_rows,Dk", [(8, 128), (9, 128), (8, 64)])
+def test_indexer_shared_prefix_rows(n_rows, Dk):
     """Rows of streams that hold the same prefix pages ([#1732] "What this changes"):
     a row group of four such streams scores each page once for all four rows (ranges
     of several pages); every logit is the oracle's. Eight rows make two such groups;
     nine add a group of one row, scored one row at a time. Rows 1, 3 and 6 stop
     inside the prefix, so the shared path masks per row; the last key range
     holds the last shared page and the streams' private tail pages, which the four
-    rows score one at a time."""
-    wl = shared_prefix_decode(0, n_streams=9, n_caches=1, shared_pages=601)
-    _log(f"indexer: shared prefix, {wl.n_pages} pages, {n_rows} rows")
+    rows score one at a time. Keys of 64 and 128 values."""
+    wl = dataclasses.replace(shared_prefix_decode(0, n_streams=9, n_caches=1, shared_pages=601), Dk=Dk)
+    _log(f"indexer: shared prefix, {wl.n_pages} pages, {n_rows} rows, Dk={Dk}")
     plan = tf.kv_pool_plan(tf.geom(1, wl.Dk))
     P = alloc_pool(wl, plan)
     populate(P)
