@@ -109,6 +109,39 @@ def test_indexer_shared_prefix_rows(n_rows, Dk):
     check_logits(host(logits), ref, logits_bound(wl, 0, rows, ld, keys=keys), "shared prefix")
     assert np.array_equal(host(nv), ow.n_valid(rows, ld))
 
+
+def test_indexer_shared_prefix_bad_pages():
+    """A shared range in which one page id is outside the pool and one is -1 in every
+    stream's table (the four rows still agree on every page): the keys of those two
+    pages score NaN within each row's compressed length, as on the per-row path, and
+    every other logit is the oracle's."""
+    wl0 = shared_prefix_decode(0, n_streams=8, n_caches=1, shared_pages=601)
+    plan = tf.kv_pool_plan(tf.geom(1, wl0.Dk))
+    P = alloc_pool(wl0, plan)
+    populate(P)
+    pt = wl0.pt.copy()
+    pt[:, 100] = wl0.n_pages + 3
+    pt[:, 101] = -1
+    _log("indexer: shared prefix with pages outside the pool")
+    view = tf.view(P.pool, torch.from_numpy(pt).cuda(), wl0.pt_stride, wl0.n_pages)
+    rows = wl0.rows
+    rs, rp, iq, w, _ = query_inputs(wl0, 0, rows)
+    ld = max(t // 4 + 1 for _, t in rows)
+    logits = torch.empty((len(rows), ld), dtype=torch.float32, device="cuda")
+    tf.indexer_logits(plan, view, rs, rp, iq, w, logits)
+    torch.cuda.synchronize()
+    got = host(logits).astype(np.float64)
+    ns = wl0.shared_tokens // 4
+    shared = ow.keys_of(wl0, 0, 0, ns)
+    keys = [np.concatenate([shared, bf16_to_f64(wl0.pkey_bits(0, b, np.arange(ns, t // 4 + 1)))]) for b, t in rows]
+    ref = ow.logits(wl0, 0, rows, ld, keys=keys)
+    nan = np.zeros_like(ref, dtype=bool)
+    nan[:, 100 * 128:102 * 128] = True
+    assert np.array_equal(np.isnan(got), nan)
+    ok = ~nan
+    A = logits_bound(wl0, 0, rows, ld, keys=keys)
+    check_logits(np.where(ok, got, 0.0), np.where(ok, ref, 0.0), np.where(ok, A, 0.0), "shared prefix, bad pages")
+
 def _oracle_image_all_caches(wl, fp8):
     """The oracle's byte image of a pool holding every stream's rows and keys in every cache."""
     g = Geom(n_caches=wl.n_caches, index_dim=wl.Dk, fp8=fp8)
