@@ -113,15 +113,19 @@ def test_prefill_chunk_full():
 
 def test_shared_prefix_decode_12_caches():
     """8 streams sharing 2,048 pages (1,048,576 tokens) plus a private tail page each, 12
-    caches: every cache runs; caches 0, 5 and 11 are checked row by row."""
+    caches: every cache runs (odd caches with the logits rows padded to 16 bytes, the
+    bench's layout); caches 0, 5 and 11 are checked row by row."""
     wl = shared_prefix_decode(0)
     plan = tf.kv_pool_plan(tf.geom(wl.n_caches, wl.Dk))
     _log(f"shared prefix: pool {wl.n_pages} pages x {plan.page_bytes} B")
     P = alloc_pool(wl, plan)
     populate(P)
     rows = wl.rows
-    ld = max(t // 4 + 1 for _, t in rows)
+    ld0 = max(t // 4 + 1 for _, t in rows)
     for c in range(wl.n_caches):
+        # odd caches: the logits rows padded to 16 bytes, as the bench lays them out (top-k's
+        # 16-byte loads); even caches: the rows' own length (its 4-byte loads)
+        ld = (ld0 + 3) // 4 * 4 if c % 2 else ld0
         lg_t, nv, blk, outs = gpu_step(plan, P.view(c), wl, c, rows, ld, [24.0])
         lg = host(lg_t)
         assert np.array_equal(blk, topk_on_values(lg, nv, wl.k)), f"cache {c}"
